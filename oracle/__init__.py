@@ -1,0 +1,29 @@
+"""CPU fp64 oracle for exact attention -- test infrastructure, not product code.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this package.  It shares no code with the HIP path: it computes the
+plain, materialising definition of scaled dot-product attention in float64
+with NumPy, one (sequence, query head) at a time.
+
+Sources (page title, section):
+  * "Deep Dive - FlashAttention": "Exact attention without an n x n workspace",
+    "Two tiles by hand", "The public interface is several kernels",
+    "Causal 2.1 is the decode gotcha", "Paged KV is a lookup, not a cache manager".
+  * "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)":
+    "Runnable Example: Measuring the IO Gap", "Decode-Time Kernels".
+  * "Flash Attention: A Complete Architectural Autopsy": "Part 1".
+  * "FlashAttention: Part 1": sections 2.2, 3.5, 4.1.
+
+Parity status: every function here is pinned by the tests in
+tests/test_oracle_pins.py except two conventions the pages leave open (the
+lse of a row with no allowed key, and the packed [Hq, total_q] lse layout of
+variable-length batches); those two are "parity unpinned".
+"""
+from .attention import (  # noqa: F401
+    kv_head_for_queries,
+    causal_keep,
+    attention_ref,
+    attention_rows,
+    paged_gather,
+    decode_ref,
+)

@@ -1,0 +1,217 @@
+"""Plain fp64 attention: the definition, materialised, on the CPU.
+
+Test infrastructure only (see the package docstring).  Nothing here is blocked,
+fused or reordered beyond the definition: for one query head h and its key/value
+head, S = scale * Q K^T, masked entries set to -inf, P = softmax over each row,
+out = P V and lse = log of the row's sum of exp(S).  Rows are processed in
+blocks of at most ROW_BLOCK rows only to bound memory; softmax is row-wise, so
+blocking rows leaves every row's result unchanged.
+"""
+import numpy as np
+
+ROW_BLOCK = 2048
+
+
+def kv_head_for_queries(num_heads_q, num_heads_kv):
+    """Map each query head to its key/value head.
+
+    "Deep Dive - FlashAttention", "The public interface is several kernels":
+    consecutive groups of query heads share one K/V head (six Q heads over two
+    K/V heads map as 0,0,0,1,1,1), and the head counts must be positive with
+    the K/V count dividing the Q count ("FlashAttention: Part 1", section 4.1).
+    """
+    for h in (num_heads_q, num_heads_kv):
+        if type(h) is not int or h <= 0:
+            raise ValueError("head counts must be positive integers")
+    if num_heads_q % num_heads_kv:
+        raise ValueError("K/V head count must divide the query head count")
+    group = num_heads_q // num_heads_kv
+    return [hq // group for hq in range(num_heads_q)]
+
+
+def causal_keep(seqlen_q, seqlen_k):
+    """Bottom-right aligned causal keep-mask, shape [seqlen_q, seqlen_k].
+
+    "Deep Dive - FlashAttention", "Causal 2.1 is the decode gotcha": from
+    FlashAttention 2.1 on, query row i may see key j exactly when
+    j <= i + seqlen_k - seqlen_q.  Rows with no allowed key exist when
+    seqlen_q > seqlen_k.
+    """
+    i = np.arange(seqlen_q)[:, None]
+    j = np.arange(seqlen_k)[None, :]
+    return j <= i + (seqlen_k - seqlen_q)
+
+
+def _attend_rows(Q, K, V, scale, keep):
+    """Attention for a block of query rows against one key/value head.
+
+    Q [n, d], K [m, d], V [m, dv] float64; keep [n, m] bool or None.
+    Returns out [n, dv] and lse [n] (natural log).
+
+    Softmax is taken in its numerically safe form, exp(x - max) / sum exp(x - max)
+    ("FlashAttention: Part 1", section 2.2; "Flash Attention: A Complete
+    Architectural Autopsy", "The Online Softmax Recurrence").  lse_i = m_i +
+    log(l_i) ("Deep Dive - FlashAttention", "Exact attention without an n x n
+    workspace").  A row with no allowed key returns out = 0 ("Deep Dive -
+    FlashAttention", "Online softmax is what makes the tiles exact") and
+    lse = -inf, the log of an empty sum (a reading: the pages define lse only
+    for non-empty rows).
+    """
+    n, m = Q.shape[0], K.shape[0]
+    dv = V.shape[1]
+    if m == 0:
+        return np.zeros((n, dv)), np.full(n, -np.inf)
+    S = scale * (Q @ K.T)
+    if keep is not None:
+        S = np.where(keep, S, -np.inf)
+    row_max = S.max(axis=1)
+    nonempty = np.isfinite(row_max)
+    shift = np.where(nonempty, row_max, 0.0)
+    E = np.exp(S - shift[:, None])
+    l = E.sum(axis=1)
+    P = E / np.where(nonempty, l, 1.0)[:, None]
+    out = P @ V
+    out[~nonempty] = 0.0
+    with np.errstate(divide="ignore"):
+        lse = np.where(nonempty, row_max + np.log(np.where(nonempty, l, 1.0)), -np.inf)
+    return out, lse
+
+
+def _as64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _sequences(cu_seqlens_q, cu_seqlens_k, batch, nq, nk):
+    """Yield (seq index, q row offset, Nq, k row offset, Nk)."""
+    if cu_seqlens_q is None:
+        for b in range(batch):
+            yield b, 0, nq, 0, nk
+    else:
+        cq = [int(x) for x in np.asarray(cu_seqlens_q)]
+        ck = [int(x) for x in np.asarray(cu_seqlens_k)]
+        for b in range(len(cq) - 1):
+            yield b, cq[b], cq[b + 1] - cq[b], ck[b], ck[b + 1] - ck[b]
+
+
+def attention_ref(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None):
+    """Full forward: (out, lse) in float64.
+
+    Dense layout ("Deep Dive - FlashAttention", "The public interface is
+    several kernels"): q [B, Nq, Hq, d], k and v [B, Nk, Hkv, d];
+    returns out [B, Nq, Hq, d] and lse [B, Hq, Nq].
+
+    Packed variable-length layout (same page, "Paged KV is a lookup, not a
+    cache manager"): q [total_q, Hq, d], k and v [total_k, Hkv, d] with int32
+    cumulative offsets cu_seqlens_q / cu_seqlens_k of batch + 1 entries;
+    returns out [total_q, Hq, d] and lse [Hq, total_q].  Causal masking is
+    bottom-right aligned per sequence, with that sequence's own lengths.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    varlen = cu_seqlens_q is not None
+    if varlen != (cu_seqlens_k is not None):
+        raise ValueError("give both cu_seqlens arrays or neither")
+    if varlen:
+        q4, k4, v4 = q[None], k[None], v[None]
+    else:
+        q4, k4, v4 = q, k, v
+    hq_n, hkv_n = q4.shape[2], k4.shape[2]
+    kvmap = kv_head_for_queries(hq_n, hkv_n)
+    out = np.zeros(q4.shape[:3] + (v4.shape[3],))
+    lse = np.full((q4.shape[0], hq_n, q4.shape[1]), -np.inf)
+    for b, qo, nq, ko, nk in _sequences(cu_seqlens_q, cu_seqlens_k, q4.shape[0], q4.shape[1], k4.shape[1]):
+        bb = 0 if varlen else b
+        for h in range(hq_n):
+            K = k4[bb, ko:ko + nk, kvmap[h], :]
+            V = v4[bb, ko:ko + nk, kvmap[h], :]
+            for r0 in range(0, nq, ROW_BLOCK):
+                r1 = min(nq, r0 + ROW_BLOCK)
+                keep = causal_keep(nq, nk)[r0:r1] if causal else None
+                o, s = _attend_rows(q4[bb, qo + r0:qo + r1, h, :], K, V, softmax_scale, keep)
+                out[bb, qo + r0:qo + r1, h, :] = o
+                lse[bb, h, qo + r0:qo + r1] = s
+    if varlen:
+        return out[0], lse[0]
+    return out, lse
+
+
+def attention_rows(q, k, v, rows, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None):
+    """The same definition evaluated for selected outputs only.
+
+    rows: iterable of (seq, q_head, i) with i the row index inside the
+    sequence.  Returns out [len(rows), d] and lse [len(rows)].  Used to check
+    full-size launches on a sample of rows; each row is computed on its own.
+    """
+    varlen = cu_seqlens_q is not None
+    kvmap = kv_head_for_queries(q.shape[-2], k.shape[-2])
+    seqs = {s[0]: s for s in _sequences(cu_seqlens_q, cu_seqlens_k,
+                                         1 if varlen else q.shape[0],
+                                         None if varlen else q.shape[1],
+                                         None if varlen else k.shape[1])}
+    outs, lses = [], []
+    for b, h, i in rows:
+        _, qo, nq, ko, nk = seqs[b]
+        if varlen:
+            Q = _as64(q[qo + i, h, :])[None]
+            K = _as64(k[ko:ko + nk, kvmap[h], :])
+            V = _as64(v[ko:ko + nk, kvmap[h], :])
+        else:
+            Q = _as64(q[b, i, h, :])[None]
+            K = _as64(k[b, :, kvmap[h], :])
+            V = _as64(v[b, :, kvmap[h], :])
+        keep = causal_keep(nq, nk)[i:i + 1] if causal else None
+        o, s = _attend_rows(Q, K, V, softmax_scale, keep)
+        outs.append(o[0])
+        lses.append(s[0])
+    return np.array(outs), np.array(lses)
+
+
+def paged_gather(cache, table_row, length):
+    """Logical rows 0..length-1 of one request from a paged cache.
+
+    "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)",
+    "Block tables and what the kernel does" and "Runnable Example": logical
+    token t lives in physical page table_row[t // page_size] at offset
+    t % page_size; the pages are concatenated in table order and cut to the
+    used length.  cache has shape [num_pages, page_size, ...].
+    """
+    page = cache.shape[1]
+    n_pages = -(-length // page)
+    if n_pages == 0:
+        return cache[:0, 0]
+    rows = np.concatenate([np.asarray(cache[int(p)]) for p in table_row[:n_pages]], axis=0)
+    return rows[:length]
+
+
+def decode_ref(q, k_cache, v_cache, block_table, seqlens_k, *, softmax_scale, requests=None):
+    """One-token decode over a paged cache, computed unsplit.
+
+    q [B, Hq, d]; k_cache and v_cache [num_pages, page_size, Hkv, d];
+    block_table int [B, max_pages]; seqlens_k int [B].  Returns out [B, Hq, d]
+    and lse [B, Hq] (or only the listed requests, in order).  With one query
+    row a bottom-right causal mask keeps every cached key ("Deep Dive -
+    FlashAttention", "Review questions"), so no mask is applied.  The split
+    into chunks and their combination is deliberately not modelled here.
+    """
+    hq_n, hkv_n = q.shape[1], k_cache.shape[2]
+    kvmap = kv_head_for_queries(hq_n, hkv_n)
+    req = range(q.shape[0]) if requests is None else list(requests)
+    out = np.zeros((len(req), hq_n, v_cache.shape[3]))
+    lse = np.full((len(req), hq_n), -np.inf)
+    for n, b in enumerate(req):
+        length = int(seqlens_k[b])
+        table = [int(x) for x in np.asarray(block_table[b])]
+        for kvh in range(hkv_n):
+            K = _as64(paged_gather(k_cache[:, :, kvh, :], table, length))
+            V = _as64(paged_gather(v_cache[:, :, kvh, :], table, length))
+            heads = [h for h in range(hq_n) if kvmap[h] == kvh]
+            Q = _as64(np.stack([np.asarray(q[b, h]) for h in heads]))
+            o, s = _attend_rows(Q, K, V, softmax_scale, None)
+            out[n, heads] = o
+            lse[n, heads] = s
+    return out, lse
+
+
+__all__ = [
+    "kv_head_for_queries", "causal_keep", "attention_ref", "attention_rows",
+    "paged_gather", "decode_ref", "ROW_BLOCK",
+]

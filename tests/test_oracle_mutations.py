@@ -1,0 +1,87 @@
+"""Plant plausible mistakes in the CPU oracle and confirm that the pins catch each.
+
+Every mutant below is applied to the oracle module with monkeypatch (on the CPU
+only); the test passes when at least one pin check in tests/pins.py fails
+under the mutant, i.e. the pins would have exposed that mistake.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.attention as OA
+import pins
+
+_orig_attend = OA._attend_rows
+_orig_keep = OA.causal_keep
+_orig_seqs = OA._sequences
+_orig_gather = OA.paged_gather
+
+
+def _attend_no_normalise(Q, K, V, scale, keep):
+    S = scale * (Q @ K.T)
+    if keep is not None:
+        S = np.where(keep, S, -np.inf)
+    mx = S.max(axis=1) if K.shape[0] else np.full(Q.shape[0], -np.inf)
+    ok = np.isfinite(mx)
+    E = np.exp(S - np.where(ok, mx, 0.0)[:, None])
+    out = E @ V
+    with np.errstate(divide="ignore"):
+        lse = np.where(ok, mx + np.log(np.where(ok, E.sum(1), 1.0)), -np.inf)
+    return out, lse
+
+
+def _attend_no_max_in_lse(Q, K, V, scale, keep):
+    out, lse = _orig_attend(Q, K, V, scale, keep)
+    S = scale * (Q @ K.T)
+    if keep is not None:
+        S = np.where(keep, S, -np.inf)
+    mx = S.max(axis=1) if K.shape[0] else np.zeros(Q.shape[0])
+    return out, np.where(np.isfinite(lse), lse - np.where(np.isfinite(mx), mx, 0.0), lse)
+
+
+def _attend_empty_rows_nan(Q, K, V, scale, keep):
+    out, lse = _orig_attend(Q, K, V, scale, keep)
+    out = out.copy()
+    out[np.isneginf(lse)] = np.nan
+    return out, lse
+
+
+def _gather_off_by_one(cache, table_row, length):
+    rows = _orig_gather(cache, table_row, length + 1)
+    return rows[1:length + 1] if len(rows) > length else rows[:length]
+
+
+def _seqs_shared_k_offset(cu_q, cu_k, batch, nq, nk):
+    for b, qo, n_q, ko, n_k in _orig_seqs(cu_q, cu_k, batch, nq, nk):
+        yield b, qo, n_q, 0, n_k
+
+
+MUTANTS = {
+    "top_left_causal": ("causal_keep", lambda nq, nk: np.arange(nk)[None, :] <= np.arange(nq)[:, None]),
+    "bottom_right_off_by_one": ("causal_keep", lambda nq, nk: np.arange(nk)[None, :] < np.arange(nq)[:, None] + nk - nq),
+    "alternating_gqa": ("kv_head_for_queries", lambda hq, hkv: [h % hkv for h in range(hq)]),
+    "scale_dropped": ("_attend_rows", lambda Q, K, V, s, keep: _orig_attend(Q, K, V, 1.0, keep)),
+    "scale_squared": ("_attend_rows", lambda Q, K, V, s, keep: _orig_attend(Q, K, V, s * s, keep)),
+    "values_reversed": ("_attend_rows", lambda Q, K, V, s, keep: _orig_attend(Q, K, V[::-1], s, keep)),
+    "keys_reversed": ("_attend_rows", lambda Q, K, V, s, keep: _orig_attend(Q, K[::-1], V, s, keep)),
+    "lse_base2": ("_attend_rows", lambda Q, K, V, s, keep: (lambda o, l: (o, l / math.log(2)))(*_orig_attend(Q, K, V, s, keep))),
+    "no_normalisation": ("_attend_rows", _attend_no_normalise),
+    "lse_without_max": ("_attend_rows", _attend_no_max_in_lse),
+    "empty_rows_nan": ("_attend_rows", _attend_empty_rows_nan),
+    "paged_gather_off_by_one": ("paged_gather", _gather_off_by_one),
+    "varlen_k_offset_ignored": ("_sequences", _seqs_shared_k_offset),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(OA, attr, fn)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, f"no pin catches mutant {name}"
