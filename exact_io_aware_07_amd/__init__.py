@@ -1,0 +1,273 @@
+"""Exact attention for AMD MI355X (gfx950): Python binding of libattn.so.
+
+The functions below only marshal arguments (shape checks, device pointers,
+the current HIP stream) and call the C ABI declared in include/attn.h; every
+step of the computation runs in the library's HIP kernels.  There is no CPU
+or PyTorch fallback: when libattn.so is missing or fails to load, every call
+raises.
+
+    out, lse = attn_fwd(q, k, v, causal=True, softmax_scale=d ** -0.5)
+    out, lse = attn_fwd(q, k, v, cu_seqlens_q=cq, cu_seqlens_k=ck,
+                        max_seqlen_q=mq, max_seqlen_k=mk, causal=True, softmax_scale=s)
+    part_o, part_l = attn_decode_splitkv(q, k_cache, v_cache, block_table, seqlens_k,
+                                         chunk_tokens=c, num_splits=n, softmax_scale=s)
+    out, lse = attn_decode_combine(part_o, part_l, seqlens_k, chunk_tokens=c)
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "AttnError", "lib", "lib_path", "attn_fwd", "attn_decode_splitkv", "attn_decode_combine",
+    "attn_decode", "attn_decode_num_splits", "attn_decode_default_chunk",
+    "attn_decode_workspace_bytes", "attn_check_cu_seqlens", "attn_check_block_table",
+    "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libattn.so")
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_ALIAS", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_DATA",
+}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "attn_abi_version": ([], _I),
+    "attn_status_str": ([_I], ctypes.c_char_p),
+    "attn_last_error": ([], ctypes.c_char_p),
+    "attn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "attn_decode_combine": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "attn_decode_num_splits": ([_I, _I], _I),
+    "attn_decode_default_chunk": ([_I, _I, _I, _I], _I),
+    "attn_decode_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
+    "attn_check_cu_seqlens": ([_P, _I, _I, _I], _I),
+    "attn_check_block_table": ([_P, _P, _I, _I, _I, _I], _I),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from libattn.so."""
+
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded libattn.so (ctypes), raising if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(
+                f"{lib_path} is missing: build it with `python -m exact_io_aware_07_amd.build`")
+        handle = ctypes.CDLL(lib_path)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise AttnError(status, lib().attn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def attn_fwd(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None,
+             max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None, return_lse=True,
+             stream=None):
+    """Forward pass; returns (out, lse) (lse is None when return_lse is False).
+
+    Dense: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> out like q, lse [B, Hq, Nq].
+    Packed: q [TQ, Hq, d], k/v [TK, Hkv, d] with int32 cu_seqlens_q/k [B + 1]
+    and max_seqlen_q/k -> out like q, lse [Hq, TQ].
+    """
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, dev)
+    varlen = cu_seqlens_q is not None
+    if varlen != (cu_seqlens_k is not None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    if varlen:
+        _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+        _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+        if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+            raise ValueError("packed mode expects q [TQ,Hq,d] and k, v [TK,Hkv,d]")
+        if max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("packed mode needs max_seqlen_q and max_seqlen_k")
+        batch = cu_seqlens_q.numel() - 1
+        if cu_seqlens_k.numel() != batch + 1:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+        _, hq, d = q.shape
+        hkv = k.shape[1]
+        mq, mk = int(max_seqlen_q), int(max_seqlen_k)
+        lse_shape = (hq, q.shape[0])
+    else:
+        if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+            raise ValueError("dense mode expects q [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d]")
+        batch, mq, hq, d = q.shape
+        mk, hkv = k.shape[1], k.shape[2]
+        if k.shape[0] != batch:
+            raise ValueError("q and k batch sizes differ")
+        lse_shape = (batch, hq, mq)
+    if k.shape[-1] != d:
+        raise ValueError("q and k head dims differ")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if return_lse:
+        if lse is None:
+            lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+        else:
+            _need(lse, "lse", torch.float32, dev)
+            if tuple(lse.shape) != lse_shape:
+                raise ValueError(f"lse must have shape {lse_shape}")
+    else:
+        lse = None
+    if q.numel() == 0:
+        return out, lse
+    with torch.cuda.device(dev):
+        st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                            batch, mq, mk, hq, hkv, d, 1 if causal else 0, float(softmax_scale),
+                            _ptr(out), _ptr(lse), _stream(stream, dev))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_num_splits(max_seqlen_k, chunk_tokens):
+    return lib().attn_decode_num_splits(int(max_seqlen_k), int(chunk_tokens))
+
+
+def attn_decode_default_chunk(batch, num_heads_kv, max_seqlen_k, num_cus=0):
+    return lib().attn_decode_default_chunk(int(batch), int(num_heads_kv), int(max_seqlen_k),
+                                           int(num_cus))
+
+
+def attn_decode_workspace_bytes(batch, num_heads_q, head_dim, num_splits):
+    return lib().attn_decode_workspace_bytes(int(batch), int(num_heads_q), int(head_dim),
+                                             int(num_splits))
+
+
+def attn_decode_splitkv(q, k_cache, v_cache, block_table, seqlens_k, *, chunk_tokens, num_splits,
+                        softmax_scale, out_partial=None, lse_partial=None, stream=None):
+    """Split pass: q [B, Hq, d]; caches [P, 256, Hkv, d]; block_table int32 [B, maxp];
+    seqlens_k int32 [B].  Returns (out_partial [n, B, Hq, d], lse_partial [n, B, Hq])."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expects q [B,Hq,d] and caches [P,page,Hkv,d]")
+    batch, hq, d = q.shape
+    num_pages, page, hkv, dk = k_cache.shape
+    if dk != d or block_table.dim() != 2 or block_table.shape[0] != batch or seqlens_k.shape != (batch,):
+        raise ValueError("inconsistent decode shapes")
+    n = int(num_splits)
+    if out_partial is None:
+        out_partial = torch.empty((n, batch, hq, d), dtype=torch.float32, device=dev)
+    if lse_partial is None:
+        lse_partial = torch.empty((n, batch, hq), dtype=torch.float32, device=dev)
+    _need(out_partial, "out_partial", torch.float32, dev)
+    _need(lse_partial, "lse_partial", torch.float32, dev)
+    if out_partial.numel() < n * batch * hq * d or lse_partial.numel() < n * batch * hq:
+        raise ValueError("partial buffers are too small for num_splits")
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(seqlens_k), batch, hq, hkv, d, page,
+                                       block_table.shape[1], num_pages, int(chunk_tokens), n,
+                                       float(softmax_scale), _ptr(out_partial), _ptr(lse_partial),
+                                       _stream(stream, dev))
+    _check(st)
+    return out_partial, lse_partial
+
+
+def attn_decode_combine(out_partial, lse_partial, seqlens_k, *, chunk_tokens, out=None, lse=None,
+                        return_lse=True, stream=None):
+    """Combine pass: returns (out [B, Hq, d] bf16, lse [B, Hq] fp32)."""
+    dev = out_partial.device
+    _need(out_partial, "out_partial", torch.float32, dev)
+    _need(lse_partial, "lse_partial", torch.float32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    n, batch, hq, d = out_partial.shape
+    if tuple(lse_partial.shape) != (n, batch, hq):
+        raise ValueError("lse_partial must be [num_splits, B, Hq]")
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_combine(_ptr(out_partial), _ptr(lse_partial), _ptr(seqlens_k), batch,
+                                       hq, d, int(chunk_tokens), n, _ptr(out), _ptr(lse),
+                                       _stream(stream, dev))
+    _check(st)
+    return out, lse
+
+
+def attn_decode(q, k_cache, v_cache, block_table, seqlens_k, *, max_seqlen_k, softmax_scale,
+                chunk_tokens=None, stream=None):
+    """Split + combine in one call (two kernel launches on the same stream)."""
+    if chunk_tokens is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        chunk_tokens = attn_decode_default_chunk(q.shape[0], k_cache.shape[2], max_seqlen_k, cus)
+    n = max(1, attn_decode_num_splits(max_seqlen_k, chunk_tokens))
+    po, pl = attn_decode_splitkv(q, k_cache, v_cache, block_table, seqlens_k,
+                                 chunk_tokens=chunk_tokens, num_splits=n,
+                                 softmax_scale=softmax_scale, stream=stream)
+    return attn_decode_combine(po, pl, seqlens_k, chunk_tokens=chunk_tokens, stream=stream)
+
+
+def attn_check_cu_seqlens(cu_seqlens, total, max_seqlen):
+    """Host-side validator over a CPU int32 tensor; raises AttnError on bad offsets."""
+    cu = cu_seqlens.to("cpu", torch.int32).contiguous()
+    _check(lib().attn_check_cu_seqlens(_ptr(cu), cu.numel() - 1, int(total), int(max_seqlen)))
+
+
+def attn_check_block_table(block_table, seqlens_k, num_pages, page_size=256):
+    """Host-side validator over CPU copies; raises AttnError on bad page ids or lengths."""
+    t = block_table.to("cpu", torch.int32).contiguous()
+    s = seqlens_k.to("cpu", torch.int32).contiguous()
+    _check(lib().attn_check_block_table(_ptr(t), _ptr(s), t.shape[0], t.shape[1], int(num_pages),
+                                        int(page_size)))

@@ -1,0 +1,278 @@
+// Host side of the C ABI declared in include/attn.h: argument validation,
+// status reporting and kernel dispatch.  Nothing here allocates device
+// memory or synchronises; errors are returned before any launch.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+attn_status_t ok() {
+    g_last_error[0] = '\0';
+    return ATTN_OK;
+}
+
+bool head_dim_supported(int d) { return d == 64 || d == 128 || d == 256; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges; empty ranges never do).
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+attn_status_t check_scale(float s) {
+    if (!isfinite(s) || !(s > 0.0f)) return fail(ATTN_ERR_SCALE, "softmax_scale must be finite and > 0 (got %g)", s);
+    return ATTN_OK;
+}
+
+attn_status_t hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_ERR_NULL: return "ATTN_ERR_NULL";
+        case ATTN_ERR_SHAPE: return "ATTN_ERR_SHAPE";
+        case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+        case ATTN_ERR_SCALE: return "ATTN_ERR_SCALE";
+        case ATTN_ERR_ALIAS: return "ATTN_ERR_ALIAS";
+        case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+        case ATTN_ERR_DATA: return "ATTN_ERR_DATA";
+        default: return "ATTN_ERR_UNKNOWN";
+    }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                       const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k,
+                       int num_heads_q, int num_heads_kv, int head_dim, int causal,
+                       float softmax_scale, void* out, float* lse, void* stream) {
+    if (!q || !k || !v || !out) return fail(ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
+    const bool varlen = cu_seqlens_q != nullptr;
+    if (varlen != (cu_seqlens_k != nullptr))
+        return fail(ATTN_ERR_NULL, "cu_seqlens_q and cu_seqlens_k must both be NULL or both be set");
+    if (batch < 1 || max_seqlen_q < 1 || max_seqlen_k < (varlen ? 0 : 1) || num_heads_q < 1 ||
+        num_heads_kv < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d max_seqlen_q=%d max_seqlen_k=%d "
+                    "num_heads_q=%d num_heads_kv=%d", batch, max_seqlen_q, max_seqlen_k,
+                    num_heads_q, num_heads_kv);
+    if (num_heads_q % num_heads_kv)
+        return fail(ATTN_ERR_SHAPE, "num_heads_kv=%d does not divide num_heads_q=%d", num_heads_kv,
+                    num_heads_q);
+    if (!head_dim_supported(head_dim))
+        return fail(ATTN_ERR_UNSUPPORTED, "head_dim=%d not in {64,128,256}", head_dim);
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1 (got %d)", causal);
+    attn_status_t st = check_scale(softmax_scale);
+    if (st != ATTN_OK) return st;
+    // Aliasing: byte ranges are known in dense mode; packed mode knows only
+    // the start pointers on the host.
+    if (!varlen) {
+        const size_t nq = (size_t)batch * max_seqlen_q, nk = (size_t)batch * max_seqlen_k;
+        const size_t qbytes = nq * num_heads_q * head_dim * 2;
+        const size_t kbytes = nk * num_heads_kv * head_dim * 2;
+        const size_t lbytes = (size_t)batch * num_heads_q * max_seqlen_q * 4;
+        if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k, kbytes) ||
+            overlap(out, qbytes, v, kbytes) || overlap(lse, lbytes, out, qbytes) ||
+            overlap(lse, lbytes, q, qbytes) || overlap(lse, lbytes, k, kbytes) ||
+            overlap(lse, lbytes, v, kbytes))
+            return fail(ATTN_ERR_ALIAS, "out/lse overlap an input or each other");
+    } else if (out == q || out == k || out == v || (void*)lse == out || (const void*)lse == q ||
+               (const void*)lse == k || (const void*)lse == v) {
+        return fail(ATTN_ERR_ALIAS, "out/lse alias an input or each other");
+    }
+    attn::FwdParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.batch = batch;
+    p.max_q = max_seqlen_q;
+    p.max_k = max_seqlen_k;
+    p.hq = num_heads_q;
+    p.hkv = num_heads_kv;
+    p.scale = softmax_scale;
+    return hip_status(attn::launch_fwd(p, head_dim, causal != 0, varlen, static_cast<hipStream_t>(stream)),
+                      "attn_fwd launch");
+}
+
+attn_status_t attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seqlens_k, int batch,
+                                  int num_heads_q, int num_heads_kv, int head_dim, int page_size,
+                                  int max_pages_per_seq, int num_pages, int chunk_tokens,
+                                  int num_splits, float softmax_scale, float* out_partial,
+                                  float* lse_partial, void* stream) {
+    if (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !out_partial || !lse_partial)
+        return fail(ATTN_ERR_NULL, "every pointer argument of attn_decode_splitkv must be non-NULL");
+    if (batch < 1 || num_heads_q < 1 || num_heads_kv < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
+        num_splits < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d num_heads_q=%d num_heads_kv=%d "
+                    "max_pages_per_seq=%d num_pages=%d num_splits=%d", batch, num_heads_q,
+                    num_heads_kv, max_pages_per_seq, num_pages, num_splits);
+    if (num_heads_q % num_heads_kv)
+        return fail(ATTN_ERR_SHAPE, "num_heads_kv=%d does not divide num_heads_q=%d", num_heads_kv,
+                    num_heads_q);
+    if (num_heads_q / num_heads_kv > 64)
+        return fail(ATTN_ERR_UNSUPPORTED, "more than 64 query heads per K/V head");
+    if (!head_dim_supported(head_dim))
+        return fail(ATTN_ERR_UNSUPPORTED, "head_dim=%d not in {64,128,256}", head_dim);
+    if (page_size != 256) return fail(ATTN_ERR_UNSUPPORTED, "page_size must be 256 (got %d)", page_size);
+    if (chunk_tokens < page_size || chunk_tokens % page_size)
+        return fail(ATTN_ERR_UNSUPPORTED, "chunk_tokens=%d is not a positive multiple of page_size",
+                    chunk_tokens);
+    attn_status_t st = check_scale(softmax_scale);
+    if (st != ATTN_OK) return st;
+    const size_t obytes = (size_t)num_splits * batch * num_heads_q * head_dim * 4;
+    const size_t lbytes = (size_t)num_splits * batch * num_heads_q * 4;
+    if (overlap(out_partial, obytes, lse_partial, lbytes))
+        return fail(ATTN_ERR_ALIAS, "out_partial and lse_partial overlap");
+    attn::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k_cache = static_cast<const uint16_t*>(k_cache);
+    p.v_cache = static_cast<const uint16_t*>(v_cache);
+    p.block_table = block_table;
+    p.seqlens = seqlens_k;
+    p.out_part = out_partial;
+    p.lse_part = lse_partial;
+    p.batch = batch;
+    p.hq = num_heads_q;
+    p.hkv = num_heads_kv;
+    p.max_pages = max_pages_per_seq;
+    p.num_pages = num_pages;
+    p.chunk = chunk_tokens;
+    p.n_splits = num_splits;
+    p.scale = softmax_scale;
+    return hip_status(attn::launch_decode_split(p, head_dim, static_cast<hipStream_t>(stream)),
+                      "attn_decode_splitkv launch");
+}
+
+attn_status_t attn_decode_combine(const float* out_partial, const float* lse_partial,
+                                  const int32_t* seqlens_k, int batch, int num_heads_q,
+                                  int head_dim, int chunk_tokens, int num_splits, void* out,
+                                  float* lse, void* stream) {
+    if (!out_partial || !lse_partial || !seqlens_k || !out)
+        return fail(ATTN_ERR_NULL, "out_partial, lse_partial, seqlens_k and out must be non-NULL");
+    if (batch < 1 || num_heads_q < 1 || num_splits < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d num_heads_q=%d num_splits=%d",
+                    batch, num_heads_q, num_splits);
+    if (!head_dim_supported(head_dim))
+        return fail(ATTN_ERR_UNSUPPORTED, "head_dim=%d not in {64,128,256}", head_dim);
+    if (chunk_tokens < 256 || chunk_tokens % 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "chunk_tokens=%d is not a positive multiple of 256",
+                    chunk_tokens);
+    const size_t obytes = (size_t)batch * num_heads_q * head_dim * 2;
+    const size_t lbytes = (size_t)batch * num_heads_q * 4;
+    const size_t pobytes = (size_t)num_splits * batch * num_heads_q * head_dim * 4;
+    const size_t plbytes = (size_t)num_splits * batch * num_heads_q * 4;
+    if (overlap(out, obytes, out_partial, pobytes) || overlap(out, obytes, lse_partial, plbytes) ||
+        overlap(lse, lbytes, out, obytes) || overlap(lse, lbytes, out_partial, pobytes) ||
+        overlap(lse, lbytes, lse_partial, plbytes))
+        return fail(ATTN_ERR_ALIAS, "out/lse overlap the partials or each other");
+    attn::CombineParams p{};
+    p.out_part = out_partial;
+    p.lse_part = lse_partial;
+    p.seqlens = seqlens_k;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.batch = batch;
+    p.hq = num_heads_q;
+    p.chunk = chunk_tokens;
+    p.n_splits = num_splits;
+    return hip_status(attn::launch_decode_combine(p, head_dim, static_cast<hipStream_t>(stream)),
+                      "attn_decode_combine launch");
+}
+
+int attn_decode_num_splits(int max_seqlen_k, int chunk_tokens) {
+    if (max_seqlen_k <= 0 || chunk_tokens <= 0) return 0;
+    return (int)(((long)max_seqlen_k + chunk_tokens - 1) / chunk_tokens);
+}
+
+int attn_decode_default_chunk(int batch, int num_heads_kv, int max_seqlen_k, int num_cus) {
+    if (num_cus <= 0) num_cus = 256;
+    if (batch < 1) batch = 1;
+    if (num_heads_kv < 1) num_heads_kv = 1;
+    if (max_seqlen_k < 1) return 256;
+    // Aim for about four workgroups per compute unit over the longest
+    // request; keep chunks between one page and 64 pages.
+    const long units = (long)batch * num_heads_kv;
+    const long want = 4L * num_cus;
+    long splits = (want + units - 1) / units;
+    if (splits < 1) splits = 1;
+    long chunk = ((long)max_seqlen_k + splits - 1) / splits;
+    chunk = ((chunk + 255) / 256) * 256;
+    if (chunk < 256) chunk = 256;
+    if (chunk > 16384) chunk = 16384;
+    return (int)chunk;
+}
+
+size_t attn_decode_workspace_bytes(int batch, int num_heads_q, int head_dim, int num_splits) {
+    if (batch < 1 || num_heads_q < 1 || head_dim < 1 || num_splits < 1) return 0;
+    return (size_t)num_splits * batch * num_heads_q * ((size_t)head_dim + 1) * 4;
+}
+
+attn_status_t attn_check_cu_seqlens(const int32_t* cu, int batch, int total, int max_seqlen) {
+    if (!cu) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+    if (batch < 1 || total < 0) return fail(ATTN_ERR_SHAPE, "batch=%d total=%d", batch, total);
+    if (cu[0] != 0) return fail(ATTN_ERR_DATA, "cu_seqlens[0]=%d, expected 0", cu[0]);
+    for (int b = 0; b < batch; ++b) {
+        const long len = (long)cu[b + 1] - cu[b];
+        if (len < 0) return fail(ATTN_ERR_DATA, "cu_seqlens decreases at %d", b + 1);
+        if (len > max_seqlen)
+            return fail(ATTN_ERR_DATA, "sequence %d has length %ld > max_seqlen %d", b, len, max_seqlen);
+    }
+    if (cu[batch] != total)
+        return fail(ATTN_ERR_DATA, "cu_seqlens[%d]=%d, expected the packed total %d", batch, cu[batch], total);
+    return ok();
+}
+
+attn_status_t attn_check_block_table(const int32_t* table, const int32_t* seqlens, int batch,
+                                     int max_pages_per_seq, int num_pages, int page_size) {
+    if (!table || !seqlens) return fail(ATTN_ERR_NULL, "block_table and seqlens must be non-NULL");
+    if (batch < 1 || max_pages_per_seq < 1 || num_pages < 1 || page_size < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range");
+    for (int b = 0; b < batch; ++b) {
+        const long n = seqlens[b];
+        if (n < 0 || n > (long)max_pages_per_seq * page_size)
+            return fail(ATTN_ERR_DATA, "seqlens[%d]=%ld outside [0, %ld]", b, n,
+                        (long)max_pages_per_seq * page_size);
+        const long used = (n + page_size - 1) / page_size;
+        for (long i = 0; i < used; ++i) {
+            const int id = table[(long)b * max_pages_per_seq + i];
+            if (id < 0 || id >= num_pages)
+                return fail(ATTN_ERR_DATA, "block_table[%d][%ld]=%d outside [0, %d)", b, i, id, num_pages);
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Kernel parameter blocks and launchers (internal to libattn.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* cu_q;  // null in dense mode
+    const int32_t* cu_k;
+    uint16_t* out;
+    float* lse;  // may be null
+    int batch, max_q, max_k, hq, hkv;
+    int n_qtiles;  // filled in by the launcher
+    float scale;
+};
+
+struct DecodeParams {
+    const uint16_t* q;
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int32_t* block_table;
+    const int32_t* seqlens;
+    float* out_part;
+    float* lse_part;
+    int batch, hq, hkv, max_pages, num_pages, chunk, n_splits;
+    float scale;
+};
+
+struct CombineParams {
+    const float* out_part;
+    const float* lse_part;
+    const int32_t* seqlens;
+    uint16_t* out;
+    float* lse;  // may be null
+    int batch, hq, chunk, n_splits;
+};
+
+hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_decode_split(const DecodeParams& p, int head_dim, hipStream_t s);
+hipError_t launch_decode_combine(const CombineParams& p, int head_dim, hipStream_t s);
+
+}  // namespace attn

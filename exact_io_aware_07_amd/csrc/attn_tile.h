@@ -1,0 +1,207 @@
+// Device building blocks shared by the prefill and decode kernels (gfx950).
+//
+// Matrix-core layout used throughout (v_mfma_f32_32x32x16_bf16, wave64):
+//   D[32x32] += A[32x16] * B[16x32]
+//   A operand: lane l holds A[l % 32][8 * (l / 32) + 0..7]   (8 bf16, 16 bytes)
+//   B operand: lane l holds B[8 * (l / 32) + 0..7][l % 32]
+//   D result:  lane l, register r holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+//
+// Scores are formed transposed, S^T = K Q^T (A = K rows, B = Q^T), so every
+// lane owns one query row (column l % 32) and sixteen of its key scores: row
+// max and row sum are in-lane work plus one swap between the two lane halves.
+// The output is kept transposed too, O^T = V^T P^T, so the S^T registers feed
+// the B operand of the second product directly (no trip through LDS) and the
+// per-row rescale multiplies whole lanes.
+//
+// The key order inside a 32-key block is whatever makes the S^T registers a
+// valid B operand: for the 16-key step c of block kb, lane half h holds keys
+// 32*kb + 16*c + {4h..4h+3, 8+4h..8+4h+3}.  V^T is stored in LDS with the keys
+// of every 16-key group permuted (bits 2 and 3 of the key index swapped) so
+// that these eight keys are one contiguous 16-byte read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// A row's shift is only raised when a tile's maximum exceeds it by more than
+// this many powers of two, so exp2(s - shift) <= 2^8 stays far inside fp32 and
+// bf16 range; the result is the same operator whatever shift is used, because
+// numerator and denominator carry the same factor.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// v_permlane32_swap with both operands = x leaves each lane holding the pair
+// {x[l], x[l ^ 32]} (one in each result), so a symmetric op of the two
+// results combines the two halves of a query row.
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Buffer resource over [base, base + bytes); raw loads at or past `bytes`
+// return zeros (gfx9 descriptor word 3: 32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, uint32_t off) {
+    return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+// XOR swizzle of 16-byte chunks for an LDS row of NCHUNK chunks.  Rows that
+// consecutive lanes read at the same logical chunk land in distinct bank
+// groups both for 128-byte and 256-byte-per-clock LDS: rows r..r+7 map to 8
+// distinct chunks, and rows r..r+15 to 16 distinct 16-byte slots of a 256-byte
+// window.  Depends on the low four row bits only.
+template <int NCHUNK>
+__device__ __forceinline__ uint32_t swz(uint32_t row) {
+    if constexpr (NCHUNK == 4) {
+        return ((row >> 1) ^ (row >> 2)) & 3u;
+    } else if constexpr (NCHUNK == 8) {
+        return (row & 7u) ^ ((row >> 3) & 1u);
+    } else {
+        static_assert(NCHUNK >= 16, "row too short");
+        return row & 15u;
+    }
+}
+
+// Storage position of key k (0..15) inside its 16-key group of a V^T row.
+__device__ __forceinline__ uint32_t key_slot(uint32_t k) {
+    return (k & 3u) | ((k & 4u) << 1) | ((k & 8u) >> 1);
+}
+
+// One K/V tile of BC keys: global -> registers -> LDS.
+//   K is stored row-major [BC][D] (row = key), V transposed [D][BC] (row = d).
+// NT threads cooperate; loads are 16-byte and coalesced (consecutive threads
+// read consecutive chunks of one row).  Rows at or past `nvalid` are not read
+// and are stored as zeros, so masked keys can never inject NaN or Inf.
+template <int D, int BC, int NT>
+struct KVTile {
+    static constexpr int KCH = D / 8;                       // 16-byte chunks per K row
+    static constexpr int KL = (BC * KCH + NT - 1) / NT;     // K loads per thread
+    static constexpr int VITEMS = (BC / 4) * KCH;           // (4 keys x 8 d) items
+    static constexpr int VI = (VITEMS + NT - 1) / NT;       // V items per thread
+    static constexpr int VCH = BC / 8;                      // 16-byte chunks per V^T row
+    static constexpr uint32_t K_BYTES = BC * D * 2;
+    static constexpr uint32_t V_BYTES = D * BC * 2;
+    static constexpr uint32_t BYTES = K_BYTES + V_BYTES;
+    static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert((BC * KCH) % NT == 0, "K chunks must split evenly over the threads");
+
+    u32x4 kr[KL];
+    u32x4 vr[VI * 4];
+
+    // kbase/vbase point at the tile's first row; consecutive rows are
+    // `stride` elements apart.  The loads go through buffer resources whose
+    // size covers exactly the first `nvalid` rows: the hardware range check
+    // returns zeros for every row past them, without branches.
+    __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase,
+                                         long stride, int nvalid, int tid) {
+        const uint32_t sb = (uint32_t)(stride * 2);
+        const uint32_t nrec = nvalid > 0 ? (uint32_t)(nvalid < BC ? nvalid : BC) * sb : 0u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nrec);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nrec);
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            const int p = tid + i * NT;
+            const uint32_t row = p / KCH, c = p % KCH;
+            kr[i] = buffer_load16(rk, row * sb + c * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            const int item = tid + i * NT;
+            const uint32_t kg = item / KCH, dc = item % KCH;
+            if (VITEMS % NT == 0 || item < VITEMS) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vr[i * 4 + j] = buffer_load16(rv, (4 * kg + j) * sb + dc * 16);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(char* ks, char* vs, int tid) const {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) {
+            const int p = tid + i * NT;
+            if (p < BC * KCH) {
+                const uint32_t row = p / KCH, c = p % KCH;
+                *reinterpret_cast<u32x4*>(ks + row * (2 * D) + ((c ^ swz<KCH>(row)) * 16)) = kr[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            const int item = tid + i * NT;
+            if (item < VITEMS) {
+                const uint32_t kg = item / KCH, dc = item % KCH;
+                const uint32_t spos = 16 * (kg / 4) + key_slot(4 * (kg % 4));
+                const uint32_t chunk = spos / 8, within = (spos % 8) * 2;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const uint32_t a0 = vr[i * 4 + 0][pp], a1 = vr[i * 4 + 1][pp];
+                    const uint32_t a2 = vr[i * 4 + 2][pp], a3 = vr[i * 4 + 3][pp];
+                    // d even: low halves of the four keys; d odd: high halves.
+                    u32x2 ev = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+                    u32x2 od = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+                    const uint32_t d0 = 8 * dc + 2 * pp, d1 = d0 + 1;
+                    *reinterpret_cast<u32x2*>(vs + d0 * (2 * BC) + ((chunk ^ swz<VCH>(d0)) * 16) + within) = ev;
+                    *reinterpret_cast<u32x2*>(vs + d1 * (2 * BC) + ((chunk ^ swz<VCH>(d1)) * 16) + within) = od;
+                }
+            }
+        }
+    }
+};
+
+// A operand of S^T = K Q^T for key block kb (32 rows) and d-step s (16 wide).
+template <int D>
+__device__ __forceinline__ u32x4 read_k_frag(const char* ks, int kb, int s, int lane) {
+    const uint32_t row = 32 * kb + (lane & 31), h = lane >> 5;
+    return lds_read16(ks, row * (2 * D) + (((2 * s + h) ^ swz<D / 8>(row)) * 16));
+}
+
+// A operand of O^T = V^T P^T for d block db (32 rows of V^T) and the 16-key
+// step (kb, c) of the tile.
+template <int BC>
+__device__ __forceinline__ u32x4 read_vt_frag(const char* vs, int db, int kb, int c, int lane) {
+    const uint32_t row = 32 * db + (lane & 31), h = lane >> 5;
+    const uint32_t chunk = 2 * (2 * kb + c) + h;
+    return lds_read16(vs, row * (2 * BC) + ((chunk ^ swz<BC / 8>(row)) * 16));
+}
+
+// Key index (within the tile) of S^T register r of block kb for this lane.
+__device__ __forceinline__ int score_key(int kb, int r, int lane) {
+    return 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+}  // namespace attn

@@ -1,0 +1,190 @@
+/*
+ * Exact attention forward pass and split-KV paged decode for AMD MI355X (gfx950).
+ *
+ * C ABI of libattn.so.  Every tensor argument is a device pointer to memory
+ * the caller allocated; the library never allocates, frees or synchronises.
+ * Every call only validates its arguments on the host and then enqueues
+ * kernels on `stream` (a hipStream_t; NULL means the null stream), so it
+ * returns before the work is done.  Calls are stateless and may be made from
+ * several host threads at once.  No call aborts or throws: failures are
+ * reported through attn_status_t, and attn_last_error() gives the calling
+ * thread's message for its last failing call.
+ *
+ * Element types: bf16 tensors are IEEE bfloat16 stored as 16-bit words;
+ * lse and the decode partials are IEEE float32.  All tensors are dense and
+ * row-major in the layouts documented below (no strides are accepted).
+ *
+ * What is computed (the definition the results are checked against):
+ *   for each sequence and query head h, with K/V head kvh = h / (Hq / Hkv),
+ *     S = softmax_scale * Q K^T, entries outside the allowed set set to -inf,
+ *     out = softmax(S) V row by row, lse = log(sum_j exp(S_ij)) (natural log).
+ *   The causal mask is bottom-right aligned: query row i of a sequence with
+ *   Nq queries and Nk keys may see key j exactly when j <= i + Nk - Nq.
+ *   A row with no allowed key gets out = 0 and lse = -inf.
+ * Sources ("Deep Dive - FlashAttention": "Exact attention without an n x n
+ * workspace", "The public interface is several kernels", "Causal 2.1 is the
+ * decode gotcha", "Paged KV is a lookup, not a cache manager";
+ * "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)":
+ * "Decode-Time Kernels: Flash-Decoding, GQA and MLA").
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL                               */
+    ATTN_ERR_SHAPE = 2,       /* a count or length is out of range, or Hq % Hkv != 0      */
+    ATTN_ERR_UNSUPPORTED = 3, /* head_dim not in {64,128,256}, page_size != 256, bad chunk  */
+    ATTN_ERR_SCALE = 4,       /* softmax_scale is not finite or not > 0                    */
+    ATTN_ERR_ALIAS = 5,       /* an output overlaps an input or the other output           */
+    ATTN_ERR_HIP = 6,         /* the HIP runtime refused a launch (see attn_last_error)    */
+    ATTN_ERR_DATA = 7         /* a host-side validator found invalid offsets or page ids   */
+} attn_status_t;
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int attn_abi_version(void);
+
+/* Static name of a status code; never NULL. */
+const char* attn_status_str(int status);
+
+/* Message of the calling thread's last failing call ("" if none); valid
+ * until that thread's next call into the library. */
+const char* attn_last_error(void);
+
+/*
+ * attn_fwd -- prefill / chunked-prefill forward pass with online softmax.
+ *
+ * Each workgroup owns one tile of query rows of one (sequence, query head)
+ * and streams the key/value tiles past it, keeping the running row maximum,
+ * running sum and output accumulator on chip; no score matrix reaches memory
+ * ("Deep Dive - FlashAttention", "Exact attention without an n x n
+ * workspace"; "Flash Attention: A Complete Architectural Autopsy", "The
+ * Online Softmax Recurrence").  Tiles wholly above the causal boundary are
+ * skipped ("FlashAttention: Part 1", section 3.5).
+ *
+ * Dense mode (cu_seqlens_q == cu_seqlens_k == NULL):
+ *   q   [batch, max_seqlen_q, num_heads_q,  head_dim] bf16
+ *   k,v [batch, max_seqlen_k, num_heads_kv, head_dim] bf16
+ *   out [batch, max_seqlen_q, num_heads_q,  head_dim] bf16
+ *   lse [batch, num_heads_q, max_seqlen_q] float32, or NULL if not wanted
+ *   Every sequence has exactly max_seqlen_q queries and max_seqlen_k keys.
+ * Packed variable-length mode (both cu_seqlens non-NULL):
+ *   cu_seqlens_q, cu_seqlens_k: int32 device arrays of batch + 1 entries,
+ *     starting at 0, nondecreasing, ending at the packed totals TQ and TK;
+ *     sequence s owns rows [cu[s], cu[s+1]) ("Deep Dive - FlashAttention",
+ *     "Paged KV is a lookup, not a cache manager").  The same pointer may be
+ *     given twice.  max_seqlen_q / max_seqlen_k must be >= every length.
+ *   q   [TQ, num_heads_q,  head_dim] bf16,  k,v [TK, num_heads_kv, head_dim] bf16
+ *   out [TQ, num_heads_q,  head_dim] bf16,  lse [num_heads_q, TQ] float32 or NULL
+ *   The offsets are read on the device and are not validated there: offsets
+ *   that break the rules above are undefined behaviour (attn_check_cu_seqlens
+ *   checks a host copy).
+ * causal: 0 = no mask, 1 = bottom-right aligned causal mask (per sequence).
+ * Requirements: batch >= 1, max_seqlen_q >= 1, max_seqlen_k >= 0 (dense:
+ *   >= 1), num_heads_kv >= 1 dividing num_heads_q, head_dim in {64,128,256},
+ *   softmax_scale finite and > 0, out distinct from q/k/v and not overlapping
+ *   lse.  Errors are returned before anything is enqueued.
+ */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int batch, int max_seqlen_q, int max_seqlen_k,
+                       int num_heads_q, int num_heads_kv, int head_dim,
+                       int causal, float softmax_scale,
+                       void* out, float* lse, void* stream);
+
+/*
+ * attn_decode_splitkv -- one-token decode over a paged KV cache, split along
+ * the cached keys ("FlashAttention-3 and PagedAttention: IO-Aware Attention
+ * Kernels (2026)", "Why decode starves the GPU" and "How GQA and MLA reshape
+ * the problem": chunks of the cache run in parallel, each emitting a partial
+ * output and its log-sum-exp; all query heads that share a K/V head are
+ * processed together so each cache row is read once).
+ *
+ *   q            [batch, num_heads_q, head_dim] bf16 (one new token per request)
+ *   k_cache,
+ *   v_cache      [num_pages, page_size, num_heads_kv, head_dim] bf16
+ *   block_table  [batch, max_pages_per_seq] int32: logical page p of request
+ *                b lives in physical page block_table[b * max_pages_per_seq + p]
+ *                ("Deep Dive - FlashAttention", "Paged KV is a lookup, not a
+ *                cache manager")
+ *   seqlens_k    [batch] int32, cached keys per request (0 allowed)
+ *   chunk_tokens keys per split; a positive multiple of page_size
+ *   num_splits   leading dimension of the partials; must be >=
+ *                ceil(max_b seqlens_k[b] / chunk_tokens) (see
+ *                attn_decode_num_splits)
+ *   out_partial  [num_splits, batch, num_heads_q, head_dim] float32 (written)
+ *   lse_partial  [num_splits, batch, num_heads_q] float32 (written)
+ * Split c of request b covers keys [c*chunk_tokens, min(seqlens_k[b],
+ * (c+1)*chunk_tokens)); splits starting at or past seqlens_k[b] are not
+ * written.  A written partial holds the softmax-normalised output over its
+ * keys and the natural-log lse of those keys.  Cache rows at or past
+ * seqlens_k[b], and table entries past ceil(seqlens_k[b]/page_size), are
+ * never used as data, so they may hold anything, NaN included.  A page id
+ * outside [0, num_pages), or a length beyond max_pages_per_seq * page_size
+ * or num_splits * chunk_tokens, turns that request's results into NaN (it
+ * never faults).  Requirements: page_size == 256, num_heads_q / num_heads_kv
+ * <= 64, head_dim in {64,128,256}; others as attn_fwd.
+ */
+attn_status_t attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seqlens_k,
+                                  int batch, int num_heads_q, int num_heads_kv, int head_dim,
+                                  int page_size, int max_pages_per_seq, int num_pages,
+                                  int chunk_tokens, int num_splits, float softmax_scale,
+                                  float* out_partial, float* lse_partial, void* stream);
+
+/*
+ * attn_decode_combine -- merge the split partials of attn_decode_splitkv.
+ * With L = log(sum_c exp(lse_c)) over the ceil(seqlens_k[b] / chunk_tokens)
+ * written splits, out = sum_c exp(lse_c - L) * out_c and lse = L (the
+ * rescaling identity of "FlashAttention-3 and PagedAttention: IO-Aware
+ * Attention Kernels (2026)", "Why decode starves the GPU").  Only written
+ * splits are read.  A request with no keys gets out = 0 and lse = -inf.
+ *   out [batch, num_heads_q, head_dim] bf16, lse [batch, num_heads_q] float32
+ *   (lse may be NULL).  The other arguments must equal those given to the
+ *   attn_decode_splitkv call that produced the partials.
+ */
+attn_status_t attn_decode_combine(const float* out_partial, const float* lse_partial,
+                                  const int32_t* seqlens_k, int batch, int num_heads_q,
+                                  int head_dim, int chunk_tokens, int num_splits,
+                                  void* out, float* lse, void* stream);
+
+/* ceil(max_seqlen_k / chunk_tokens), the smallest valid num_splits (0 if
+ * max_seqlen_k <= 0 or chunk_tokens <= 0). */
+int attn_decode_num_splits(int max_seqlen_k, int chunk_tokens);
+
+/* A chunk size (a multiple of 256) that gives a few workgroups per compute
+ * unit for the given batch, K/V head count and longest cached length; the
+ * split count is free ("FlashAttention-3 and PagedAttention: IO-Aware
+ * Attention Kernels (2026)", "Why decode starves the GPU"), results do not
+ * depend on it beyond rounding.  num_cus <= 0 means 256. */
+int attn_decode_default_chunk(int batch, int num_heads_kv, int max_seqlen_k, int num_cus);
+
+/* Bytes of out_partial plus lse_partial for these sizes. */
+size_t attn_decode_workspace_bytes(int batch, int num_heads_q, int head_dim, int num_splits);
+
+/* Host-side validators (they read host arrays only and never touch the GPU).
+ * attn_check_cu_seqlens: cu[0] == 0, nondecreasing, cu[batch] == total, and
+ * every length <= max_seqlen.  attn_check_block_table: every used entry
+ * (ceil(seqlens[b] / page_size) per request) lies in [0, num_pages) and
+ * every seqlens[b] is in [0, max_pages_per_seq * page_size].  Both return
+ * ATTN_OK or ATTN_ERR_DATA (ATTN_ERR_NULL / ATTN_ERR_SHAPE for bad calls). */
+attn_status_t attn_check_cu_seqlens(const int32_t* cu_seqlens_host, int batch, int total,
+                                    int max_seqlen);
+attn_status_t attn_check_block_table(const int32_t* block_table_host,
+                                     const int32_t* seqlens_host, int batch,
+                                     int max_pages_per_seq, int num_pages, int page_size);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

@@ -1,0 +1,137 @@
+"""The C ABI on the host: symbols, status codes and argument validation (no GPU).
+
+Every call here fails host-side validation (or is a pure host helper), so no
+kernel is ever launched and the fake device pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import exact_io_aware_07_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x20000)
+FAKE3 = ctypes.c_void_p(0x30000)
+OUT = ctypes.c_void_p(0x40000000)
+LSE = ctypes.c_void_p(0x50000000)
+NULL = None
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ea.lib()
+    names = header_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    lib = ea.lib()
+    assert lib.attn_abi_version() == 1
+    for code, name in ea.STATUS.items():
+        assert lib.attn_status_str(code).decode() == name
+    assert lib.attn_status_str(99).decode() == "ATTN_ERR_UNKNOWN"
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, cq=NULL, ck=NULL, batch=1, mq=8, mk=8, hq=4, hkv=2, d=128,
+             causal=1, scale=0.125, out=OUT, lse=LSE)
+    a.update(kw)
+    lib = ea.lib()
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["batch"], a["mq"], a["mk"],
+                        a["hq"], a["hkv"], a["d"], a["causal"], a["scale"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(out=NULL), 1), (dict(cq=FAKE), 1),
+    (dict(batch=0), 2), (dict(mq=0), 2), (dict(mk=0), 2), (dict(hq=0), 2), (dict(hkv=0), 2),
+    (dict(hq=6, hkv=4), 2), (dict(causal=2), 2),
+    (dict(d=96), 3), (dict(d=512), 3), (dict(d=0), 3),
+    (dict(scale=0.0), 4), (dict(scale=-1.0), 4), (dict(scale=float("inf")), 4),
+    (dict(scale=float("nan")), 4),
+    (dict(out=FAKE), 5), (dict(lse=OUT), 5), (dict(out=ctypes.c_void_p(0x10000 + 64)), 5),
+])
+def test_fwd_rejects(kw, code):
+    assert fwd(**kw) == code
+    msg = ea.lib().attn_last_error().decode()
+    assert msg
+
+
+def dec(**kw):
+    a = dict(q=FAKE, kc=FAKE2, vc=FAKE3, bt=ctypes.c_void_p(0x60000), sl=ctypes.c_void_p(0x70000),
+             batch=2, hq=8, hkv=2, d=128, page=256, maxp=4, npages=8, chunk=512, nsplit=2,
+             scale=0.1, po=OUT, pl=LSE)
+    a.update(kw)
+    return ea.lib().attn_decode_splitkv(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["batch"],
+                                        a["hq"], a["hkv"], a["d"], a["page"], a["maxp"], a["npages"],
+                                        a["chunk"], a["nsplit"], a["scale"], a["po"], a["pl"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(bt=NULL), 1), (dict(sl=NULL), 1), (dict(pl=NULL), 1),
+    (dict(batch=0), 2), (dict(nsplit=0), 2), (dict(npages=0), 2), (dict(hq=6, hkv=4), 2),
+    (dict(hq=130, hkv=2), 3), (dict(page=16), 3), (dict(chunk=300), 3), (dict(chunk=0), 3),
+    (dict(d=80), 3), (dict(scale=0.0), 4), (dict(pl=ctypes.c_void_p(0x40000000 + 1024)), 5),
+])
+def test_decode_split_rejects(kw, code):
+    assert dec(**kw) == code
+
+
+def comb(**kw):
+    a = dict(po=FAKE, pl=FAKE2, sl=FAKE3, batch=2, hq=8, d=128, chunk=512, nsplit=2, out=OUT, lse=LSE)
+    a.update(kw)
+    return ea.lib().attn_decode_combine(a["po"], a["pl"], a["sl"], a["batch"], a["hq"], a["d"],
+                                        a["chunk"], a["nsplit"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(po=NULL), 1), (dict(out=NULL), 1), (dict(batch=0), 2), (dict(nsplit=0), 2),
+    (dict(d=32), 3), (dict(chunk=100), 3), (dict(out=FAKE), 5), (dict(lse=OUT), 5),
+])
+def test_decode_combine_rejects(kw, code):
+    assert comb(**kw) == code
+
+
+def test_host_helpers():
+    assert ea.attn_decode_num_splits(32768, 2048) == 16
+    assert ea.attn_decode_num_splits(32769, 2048) == 17
+    assert ea.attn_decode_num_splits(0, 256) == 0
+    for args in [(64, 8, 32768, 256), (1, 1, 100, 256), (2, 32, 1 << 20, 304)]:
+        c = ea.attn_decode_default_chunk(*args)
+        assert c >= 256 and c % 256 == 0
+    assert ea.attn_decode_workspace_bytes(64, 32, 128, 16) == 16 * 64 * 32 * 129 * 4
+
+
+def test_cu_seqlens_validator():
+    good = torch.tensor([0, 3, 3, 10], dtype=torch.int32)
+    ea.attn_check_cu_seqlens(good, total=10, max_seqlen=7)
+    for bad, total, mx in [([1, 3, 3, 10], 10, 7), ([0, 3, 2, 10], 10, 8), ([0, 3, 3, 10], 11, 7),
+                           ([0, 3, 3, 10], 10, 6)]:
+        with pytest.raises(ea.AttnError) as e:
+            ea.attn_check_cu_seqlens(torch.tensor(bad, dtype=torch.int32), total=total, max_seqlen=mx)
+        assert e.value.status == 7
+
+
+def test_block_table_validator():
+    table = torch.tensor([[3, 1, 0], [2, 9, 9]], dtype=torch.int32)
+    ea.attn_check_block_table(table, torch.tensor([700, 256], dtype=torch.int32), num_pages=4)
+    for lens in ([700, 257], [769, 10], [-1, 5]):
+        with pytest.raises(ea.AttnError) as e:
+            ea.attn_check_block_table(table, torch.tensor(lens, dtype=torch.int32), num_pages=4)
+        assert e.value.status == 7
+
+
+def test_python_binding_rejects_cpu_tensors():
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, q, q, causal=False, softmax_scale=0.125)
