@@ -1,0 +1,285 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole path over resident synthetic inputs:
+  1. attn_fwd on the causal MHA prefill workload (B=4, H=16, N=4096, d=128,
+     bf16 N(0,1)), and
+  2. attn_decode_splitkv + attn_decode_combine on the paged decode workload
+     (B=64, Hq=32, Hkv=8, d=128, 256-token pages, per-request length uniform
+     in [4096, 32768]).
+Each kernel is bracketed by HIP events recorded on the stream it is launched
+on (torch's current stream).  The headline value is the prefill throughput in
+TFLOP/s (4*Nq*Nk*d per head, halved for causal); the decode leg reports HBM
+GB/s over its algorithmic bytes (K/V rows used, q, out, lse, block table and
+lengths).  The CPU oracle is timed on a bounded sample of the prefill
+workload as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+PREFILL = "c2_causal_mha_d128"
+DECODE = "c5_splitkv_paged_decode"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["attn_tile.h", "attn_fwd.hip", "attn_decode.hip", "attn_launch.h"]
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_io_aware_07_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(case):
+    """Metric FLOPs: 4*Nq*Nk*d per (sequence, head), halved when causal."""
+    per_head = 4.0 * case["Nq"] * case["Nk"] * case["d"]
+    if case["causal"]:
+        per_head /= 2
+    return per_head * case["B"] * case["Hq"]
+
+
+def prefill_flops_exact(case):
+    """4*d per allowed (query, key) pair (bottom-right causal)."""
+    nq, nk = case["Nq"], case["Nk"]
+    if not case["causal"]:
+        pairs = nq * nk
+    else:
+        pairs = sum(max(0, min(nk, i + nk - nq + 1)) for i in range(nq))
+    return 4.0 * case["d"] * pairs * case["B"] * case["Hq"]
+
+
+def prefill_bytes(case):
+    """Compulsory traffic: read Q, K, V once; write out once and lse once."""
+    B, Nq, Nk, Hq, Hkv, d = (case[x] for x in ("B", "Nq", "Nk", "Hq", "Hkv", "d"))
+    return 2 * (2 * B * Nq * Hq * d + 2 * B * Nk * Hkv * d) + 4 * B * Hq * Nq
+
+
+def decode_bytes(case):
+    """K/V rows actually used, q, out, lse, used block-table entries and lengths."""
+    lens = case["seqlens_k"].tolist()
+    Hq, Hkv, d, page = case["Hq"], case["Hkv"], case["d"], case["page"]
+    kv = sum(lens) * Hkv * d * 2 * 2
+    qo = 2 * case["B"] * Hq * d * 2
+    lse = 4 * case["B"] * Hq
+    table = 4 * sum(-(-n // page) for n in lens) + 4 * case["B"]
+    return kv + qo + lse + table
+
+
+def load_traffic(kernel_key, digest):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != digest:
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    q, k, v = (case[x].to("cpu", dtype=torch.float32).numpy() for x in "qkv")
+    B, Hq = case["B"], case["Hq"]
+    pairs = [(b, h) for h in range(Hq) for b in range(B)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in pairs:
+        hk = h // (Hq // case["Hkv"])
+        oracle.attention_ref(q[b:b + 1, :, h:h + 1].astype(np.float64),
+                             k[b:b + 1, :, hk:hk + 1].astype(np.float64),
+                             v[b:b + 1, :, hk:hk + 1].astype(np.float64),
+                             causal=case["causal"], softmax_scale=case["scale"])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    elapsed = time.perf_counter() - t0
+    per_head = prefill_flops(case) / (B * Hq)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": per_head * done / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{done} of {B * Hq} (batch, head) pairs of {PREFILL}, each the full "
+                   f"{case['Nq']}x{case['Nk']} causal problem in fp64 NumPy (materialising S, "
+                   f"masked half included), {elapsed:.1f} s; metric FLOPs as on the GPU"),
+        "cpu": cpu,
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (for counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import exact_io_aware_07_amd as ea
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    pc = W.config_case(PREFILL, device=dev)
+    out = torch.empty_like(pc["q"])
+    lse = torch.empty((pc["B"], pc["Hq"], pc["Nq"]), dtype=torch.float32, device=dev)
+
+    dc = W.config_case(DECODE, device=dev)
+    dc_dev = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in dc.items()}
+    max_len = int(dc["seqlens_k"].max())
+    chunk = ea.attn_decode_default_chunk(dc["B"], dc["Hkv"], max_len, props.multi_processor_count)
+    n_splits = ea.attn_decode_num_splits(max_len, chunk)
+    part_o = torch.empty((n_splits, dc["B"], dc["Hq"], dc["d"]), dtype=torch.float32, device=dev)
+    part_l = torch.empty((n_splits, dc["B"], dc["Hq"]), dtype=torch.float32, device=dev)
+    dout = torch.empty((dc["B"], dc["Hq"], dc["d"]), dtype=torch.bfloat16, device=dev)
+    dlse = torch.empty((dc["B"], dc["Hq"]), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        ea.attn_fwd(pc["q"], pc["k"], pc["v"], causal=pc["causal"], softmax_scale=pc["scale"],
+                    out=out, lse=lse, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        ea.attn_decode_splitkv(dc_dev["q"], dc_dev["k_cache"], dc_dev["v_cache"],
+                               dc_dev["block_table"], dc_dev["seqlens_k"], chunk_tokens=chunk,
+                               num_splits=n_splits, softmax_scale=dc["scale"], out_partial=part_o,
+                               lse_partial=part_l, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        ea.attn_decode_combine(part_o, part_l, dc_dev["seqlens_k"], chunk_tokens=chunk, out=dout,
+                               lse=dlse, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy calibration: {n * 4} bytes read and written", file=sys.stderr, flush=True)
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre = [e[0].elapsed_time(e[1]) for e in events]
+    spl = [e[1].elapsed_time(e[2]) for e in events]
+    cmb = [e[2].elapsed_time(e[3]) for e in events]
+    mean = lambda xs: sum(xs) / len(xs)
+    pct = lambda xs, p: sorted(xs)[min(len(xs) - 1, int(round(p * (len(xs) - 1))))]
+    pre_ms, spl_ms, cmb_ms = mean(pre), mean(spl), mean(cmb)
+
+    flops = prefill_flops(pc)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    dbytes = decode_bytes(dc)
+    split_gbs = dbytes / (spl_ms * 1e-3) / 1e9
+    decode_gbs = dbytes / ((spl_ms + cmb_ms) * 1e-3) / 1e9
+    digest = source_digest()
+    pre_traffic = load_traffic("attn_fwd_kernel", digest)
+    dec_traffic = load_traffic("attn_decode_split_kernel", digest)
+
+    rec = {
+        "metric": "attn fwd TFLOP/s (bf16 d=128 causal, % MFMA peak); decode HBM GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PREFILL, "B": pc["B"], "Hq": pc["Hq"], "Hkv": pc["Hkv"],
+                   "Nq": pc["Nq"], "Nk": pc["Nk"], "d": pc["d"], "causal": pc["causal"],
+                   "decode_workload": DECODE, "decode_chunk_tokens": chunk,
+                   "decode_splits": n_splits},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": pre_traffic},
+        "prefill": {"kernel_ms_mean": round(pre_ms, 4), "kernel_ms_p50": round(pct(pre, 0.5), 4),
+                    "kernel_ms_p95": round(pct(pre, 0.95), 4), "flops_metric": flops,
+                    "flops_exact": prefill_flops_exact(pc),
+                    "tflops_exact": round(prefill_flops_exact(pc) / (pre_ms * 1e-3) / 1e12, 2),
+                    "algorithmic_bytes": prefill_bytes(pc)},
+        "decode": {"value": round(decode_gbs, 1), "unit": "GB/s",
+                   "split_ms_mean": round(spl_ms, 4), "combine_ms_mean": round(cmb_ms, 4),
+                   "split_ms_p95": round(pct(spl, 0.95), 4),
+                   "algorithmic_bytes": dbytes,
+                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": dec_traffic}},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count, "torch": torch.__version__,
+                   "hip": getattr(torch.version, "hip", None)},
+        "kernel_source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(pc)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
