@@ -41,7 +41,12 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecodeParams
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int l32 = lane & 31;
-    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    // The K/V heads of one (request, chunk) are consecutive workgroups: their
+    // rows interleave in the same cache pages, so they read those pages at
+    // about the same time.
+    const int kvh = blockIdx.x % p.hkv;
+    const int split = (blockIdx.x / p.hkv) % p.n_splits;
+    const int b = blockIdx.x / (p.hkv * p.n_splits);
     const int g = p.hq / p.hkv;
     const int hq0 = kvh * g;
 
@@ -306,14 +311,20 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(CombineParams p
 template <int D, int QB, int NW>
 static hipError_t launch_split_cfg(const DecodeParams& p, hipStream_t s) {
     if (p.n_splits <= 0 || p.batch <= 0) return hipSuccess;
-    hipLaunchKernelGGL((attn_decode_split_kernel<D, QB, NW>), dim3(p.n_splits, p.hkv, p.batch),
-                       dim3(NW * 64), 0, s, p);
+    const long grid = (long)p.n_splits * p.hkv * p.batch;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, QB, NW>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       s, p);
     return hipGetLastError();
 }
 
+#ifndef ATTN_DEC_NW
+#define ATTN_DEC_NW 2
+#endif
+
 template <int D>
 static hipError_t launch_split_d(const DecodeParams& p, hipStream_t s) {
-    constexpr int NW = D >= 256 ? 2 : 4;
+    constexpr int NW = D >= 256 ? 2 : ATTN_DEC_NW;
     const int g = p.hq / p.hkv;
     return g <= 32 ? launch_split_cfg<D, 1, NW>(p, s) : launch_split_cfg<D, 2, NW>(p, s);
 }

@@ -27,16 +27,22 @@
 
 namespace attn {
 
-template <int D, int QB, int BC, int NW, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
+template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_fwd_kernel(FwdParams p) {
     constexpr int NT = NW * 64;
     constexpr int ROWS_W = 32 * QB;
     constexpr int BR = NW * ROWS_W;
     constexpr int KB = BC / 32;  // 32-key blocks per tile
     constexpr int DB = D / 32;   // 32-wide d blocks of O^T
     constexpr int KS = D / 16;   // 16-wide d steps of S^T
-    using Tile = KVTile<D, BC, NT>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * Tile::BYTES];
+    using Tile = KVDirect<D, BC, NW>;
+    // Two LDS stages as distinct objects, and a loop unrolled by two so that
+    // every access names its stage statically: the compiler can then see that
+    // the next tile's LDS-DMA writes never alias the reads of the current
+    // tile, and does not wait for them before those reads.
+    __shared__ __attribute__((aligned(1024))) char stage0[Tile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage1[Tile::BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -87,6 +93,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
     }
 
     const long kv_stride = (long)p.hkv * D;
+    const uint32_t stride_b = (uint32_t)(kv_stride * 2);
     const uint16_t* kbase = p.k + ((long)k_off * p.hkv + kvh) * D;
     const uint16_t* vbase = p.v + ((long)k_off * p.hkv + kvh) * D;
 
@@ -125,19 +132,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
     }
     const float c2 = p.scale * kLog2e;
 
-    Tile tile;
-    if (n_tiles > 0) {
-        tile.load(kbase, vbase, kv_stride, Nk, tid);
-        tile.store(smem, smem + Tile::K_BYTES, tid);
-    }
+    if (n_tiles > 0) Tile::issue(kbase, vbase, stride_b, Nk, stage0, wave, lane);
+    wait_vmem();
     __syncthreads();
 
-    for (int t = 0; t < n_tiles; ++t) {
-        char* ks = smem + (t & 1) * Tile::BYTES;
-        char* vs = ks + Tile::K_BYTES;
+    auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
+        const char* ks = cur;
+        const char* vs = cur + Tile::K_BYTES;
         if (t + 1 < n_tiles) {
             const long off = (long)(t + 1) * BC * kv_stride;
-            tile.load(kbase + off, vbase + off, kv_stride, Nk - (t + 1) * BC, tid);
+            Tile::issue(kbase + off, vbase + off, stride_b, Nk - (t + 1) * BC, nxt, wave, lane);
         }
         const int k0 = t * BC;
         const bool active = wave_rows && (!CAUSAL || k0 <= w_last_key);
@@ -224,16 +228,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const u32x4 a = read_vt_frag<BC>(vs, db, kb, c, lane);
+                        const u32x4 a = read_vt_frag_tr<D>(vs, db, kb, c, lane);
 #pragma unroll
                         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(a, pb[kb][qb][c], oacc[db][qb]);
                     }
         }
-        if (t + 1 < n_tiles) {
-            char* nks = smem + ((t + 1) & 1) * Tile::BYTES;
-            tile.store(nks, nks + Tile::K_BYTES, tid);
-        }
+        // The next tile's loads (this wave's share) must have landed in LDS
+        // before the barrier releases other waves to read them.
+        wait_vmem();
         __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, stage0, stage1);
+        if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
     }
 
     // ---- epilogue: out = O / l (bf16, round to nearest even), lse in nats ----
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, int QB, int BC, int NW, bool CAUSAL, bool VARLEN>
+template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN>
 static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     FwdParams p = p0;
     constexpr int BR = NW * 32 * QB;
@@ -273,26 +280,38 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     const long grid = (long)p.n_qtiles * p.batch * p.hq;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, CAUSAL, VARLEN>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, WPE, CAUSAL, VARLEN>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, int QB, int BC, int NW>
+template <int D, int QB, int BC, int NW, int WPE>
 static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, hipStream_t s) {
     if (causal) {
-        return varlen ? launch_fwd_cfg<D, QB, BC, NW, true, true>(p, s)
-                      : launch_fwd_cfg<D, QB, BC, NW, true, false>(p, s);
+        return varlen ? launch_fwd_cfg<D, QB, BC, NW, WPE, true, true>(p, s)
+                      : launch_fwd_cfg<D, QB, BC, NW, WPE, true, false>(p, s);
     }
-    return varlen ? launch_fwd_cfg<D, QB, BC, NW, false, true>(p, s)
-                  : launch_fwd_cfg<D, QB, BC, NW, false, false>(p, s);
+    return varlen ? launch_fwd_cfg<D, QB, BC, NW, WPE, false, true>(p, s)
+                  : launch_fwd_cfg<D, QB, BC, NW, WPE, false, false>(p, s);
 }
+
+// Tile shapes per head dim: <QB (32-row blocks per wave), BC (keys per tile),
+// NW (waves per workgroup), WPE (waves per SIMD the register budget targets)>.
+#ifndef ATTN_FWD128_CFG
+#define ATTN_FWD128_CFG 1, 64, 8, 2
+#endif
+#ifndef ATTN_FWD64_CFG
+#define ATTN_FWD64_CFG 2, 64, 4, 1
+#endif
+#ifndef ATTN_FWD256_CFG
+#define ATTN_FWD256_CFG 1, 32, 4, 1
+#endif
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_fwd_d<64, 2, 64, 4>(p, causal, varlen, s);
-        case 128: return launch_fwd_d<128, 1, 64, 4>(p, causal, varlen, s);
-        case 256: return launch_fwd_d<256, 1, 32, 4>(p, causal, varlen, s);
+        case 64: return launch_fwd_d<64, ATTN_FWD64_CFG>(p, causal, varlen, s);
+        case 128: return launch_fwd_d<128, ATTN_FWD128_CFG>(p, causal, varlen, s);
+        case 256: return launch_fwd_d<256, ATTN_FWD256_CFG>(p, causal, varlen, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -183,6 +183,97 @@ struct KVTile {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS tiles (no register staging).
+//
+// K and V tiles are both stored row-major [BC][D] (row = key), 16-byte chunks
+// XOR-swizzled per row.  A 16-byte buffer load with the LDS flag writes the 64
+// lanes' data to 1 KiB of LDS in lane order at a wave-uniform base, so each
+// lane fetches whichever global chunk belongs at its LDS slot; 16 consecutive
+// lanes still cover one 256-byte row, so the reads stay coalesced.  Rows past
+// the resource size (keys past the end) arrive as zeros.
+//
+// V is read back transposed with ds_read_b64_tr_b16.  Within each group of 16
+// lanes that instruction hands output lane j, element k, the element (j % 4)
+// of the 8 bytes addressed by source lane 4k + j / 4.  So when source lane s
+// addresses V[key0 + s / 4][d0 + 4 * (s % 4) .. +3], output lane j receives
+// V[key0 .. key0 + 3][d0 + j]: four consecutive keys of one d column, i.e. half
+// of a V^T A-operand fragment.
+
+using lds_ptr_t = __attribute__((address_space(3))) void*;
+
+// Wait until every vector memory operation of this wave has completed
+// (s_waitcnt vmcnt(0); exp and lgkm counters left unconstrained).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char* lds_base,
+                                                  uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_ptr_t)(__attribute__((address_space(3))) char*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// Swizzle for V rows read by ds_read_b64_tr_b16: one instruction touches 8
+// consecutive key rows and a 64-byte window of each; this spreads the eight
+// windows evenly over the banks (two per 64-byte bank group).
+template <int NCHUNK>
+__device__ __forceinline__ uint32_t swz_tr(uint32_t row) {
+    if constexpr (NCHUNK == 8) {
+        return 4u * ((row >> 1) & 1u);
+    } else {
+        static_assert(NCHUNK >= 16, "row too short");
+        return 4u * (row & 3u);
+    }
+}
+
+template <int D, int BC, int NW>
+struct KVDirect {
+    static constexpr uint32_t ROWB = D * 2;        // bytes per row
+    static constexpr int CH = D / 8;               // 16-byte chunks per row
+    static constexpr uint32_t K_BYTES = BC * ROWB;
+    static constexpr uint32_t BYTES = 2 * K_BYTES; // K then V
+    static constexpr int INSTR = K_BYTES / 1024;   // 1 KiB load instructions per tensor
+    static constexpr int PER_WAVE = INSTR / NW;
+    static constexpr int RPI = 1024 / ROWB;        // rows per instruction
+    static_assert(INSTR % NW == 0, "each wave issues the same number of loads");
+
+    // Issue this wave's share of the loads of one tile into stage `st`.
+    // kbase/vbase: first row of the tile; consecutive rows `stride_b` bytes
+    // apart; the first `nvalid` rows are real keys.
+    __device__ __forceinline__ static void issue(const uint16_t* kbase, const uint16_t* vbase,
+                                                 uint32_t stride_b, int nvalid, char* st,
+                                                 int wave, int lane) {
+        const uint32_t nrec = nvalid > 0 ? (uint32_t)(nvalid < BC ? nvalid : BC) * stride_b : 0u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nrec);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nrec);
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int i = wave * PER_WAVE + j;
+            const uint32_t row = i * RPI + lane / CH;
+            const uint32_t pc = lane % CH;
+            buffer_load_lds16(rk, st + i * 1024, row * stride_b + ((pc ^ swz<CH>(row)) * 16));
+            buffer_load_lds16(rv, st + K_BYTES + i * 1024, row * stride_b + ((pc ^ swz_tr<CH>(row)) * 16));
+        }
+    }
+};
+
+// A operand of O^T = V^T P^T from a row-major V tile (see KVDirect).
+template <int D>
+__device__ __forceinline__ u32x4 read_vt_frag_tr(const char* vs, int db, int kb, int c, int lane) {
+    constexpr int CH = D / 8;
+    const uint32_t G = lane >> 4, s = lane & 15;
+    const uint32_t d = 32 * db + 16 * (G & 1) + 4 * (s & 3);
+    const uint32_t key = 32 * kb + 16 * c + 4 * (G >> 1) + (s >> 2);
+    const uint32_t k2 = key + 8;
+    const uint32_t a1 = key * (2 * D) + (((d >> 3) ^ swz_tr<CH>(key)) * 16) + (d & 7) * 2;
+    const uint32_t a2 = k2 * (2 * D) + (((d >> 3) ^ swz_tr<CH>(k2)) * 16) + (d & 7) * 2;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)(vs + a1));
+    const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)(vs + a2));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
+    return u32x4{w1[0], w1[1], w2[0], w2[1]};
+}
+
 // A operand of S^T = K Q^T for key block kb (32 rows) and d-step s (16 wide).
 template <int D>
 __device__ __forceinline__ u32x4 read_k_frag(const char* ks, int kb, int s, int lane) {
