@@ -27,6 +27,11 @@
 
 namespace attn {
 
+// K fragment reads issued ahead of the first score MFMA of a tile.
+#ifndef ATTN_FWD_K_LEAD
+#define ATTN_FWD_K_LEAD 8
+#endif
+
 template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdParams p) {
@@ -163,6 +168,15 @@ void attn_fwd_kernel(FwdParams p) {
                     for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma32(a, qf[qb][s], sacc[kb][qb]);
                 }
             }
+            // Keep the K fragment reads ATTN_FWD_K_LEAD MFMAs ahead of their
+            // use so that LDS latency is not exposed before each MFMA.
+            __builtin_amdgcn_sched_group_barrier(0x100, ATTN_FWD_K_LEAD, 0);  // DS read
+#pragma unroll
+            for (int i = 0; i < KS * KB - ATTN_FWD_K_LEAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, QB * ATTN_FWD_K_LEAD, 0);
             // ---- mask: only tiles crossing the diagonal or the key end ----
             const bool need_mask =
                 (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > w_first_key_lim);
