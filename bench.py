@@ -28,8 +28,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
-PREFILL = "c2_causal_mha_d128"
-DECODE = "c5_splitkv_paged_decode"
+PREFILL = "mha_causal_b4_h16_n4096_d128"
+DECODE = "paged_decode_b64_hq32_hkv8_d128"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["attn_tile.h", "attn_fwd.hip", "attn_decode.hip", "attn_launch.h"]
 
@@ -152,7 +152,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
     if args.steps < 1:

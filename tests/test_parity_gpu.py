@@ -85,7 +85,7 @@ def test_dense_small(shape):
 
 
 def test_config_noncausal_mha_full():
-    c = W.CONFIGS["c1_noncausal_mha_d64"]
+    c = W.CONFIGS["mha_noncausal_b1_h4_n512_d64"]
     dense_parity(c["B"], c["Nq"], c["Nk"], c["Hq"], c["Hkv"], c["d"], c["causal"], c["seed"])
 
 
@@ -98,7 +98,7 @@ def sample_dense_rows(B, Hq, Nq, n, seed):
     return sorted(r for r in rows if r[2] < Nq)
 
 
-@pytest.mark.parametrize("name", ["c2_causal_mha_d128", "c3_causal_gqa_d128_outliers"])
+@pytest.mark.parametrize("name", ["mha_causal_b4_h16_n4096_d128", "gqa_causal_b2_hq32_hkv8_n8192_d128_koutliers"])
 def test_config_dense_full_sampled(name):
     case = W.config_case(name, device=DEV)
     out, lse = ea.attn_fwd(case["q"], case["k"], case["v"], causal=case["causal"],
@@ -175,7 +175,7 @@ def test_varlen_small_edge_lengths(d):
 
 @pytest.mark.parametrize("d", [128, 64, 256])
 def test_config_varlen_chunked_prefill_sampled(d):
-    c = W.CONFIGS["c4_varlen_chunked_prefill"]
+    c = W.CONFIGS["varlen_chunked_prefill_16seq_hq32_hkv8"]
     nq, nk = W.varlen_lengths(c["n_seqs"], c["nk_lo"], c["nk_hi"], c["q_div"], c["seed"])
     varlen_parity(nq, nk, c["Hq"], c["Hkv"], d, True, seed=c["seed"] * 1000 + d, sample=64)
 
@@ -238,7 +238,7 @@ def test_decode_mqa_and_wide_groups():
 
 
 def test_config_decode_full_sampled():
-    case = W.config_case("c5_splitkv_paged_decode", device=DEV)
+    case = W.config_case("paged_decode_b64_hq32_hkv8_d128", device=DEV)
     lens = case["seqlens_k"].tolist()
     order = np.argsort(lens)
     req = sorted({int(order[0]), int(order[-1]), 5, 17, 40})

@@ -16,16 +16,16 @@ PAGE_SIZE = 256
 
 # The five workloads (shapes, masks, head layouts and length mixes).
 CONFIGS = {
-    "c1_noncausal_mha_d64": dict(kind="dense", B=1, Hq=4, Hkv=4, Nq=512, Nk=512, d=64,
+    "mha_noncausal_b1_h4_n512_d64": dict(kind="dense", B=1, Hq=4, Hkv=4, Nq=512, Nk=512, d=64,
                                  causal=False, seed=1),
-    "c2_causal_mha_d128": dict(kind="dense", B=4, Hq=16, Hkv=16, Nq=4096, Nk=4096, d=128,
+    "mha_causal_b4_h16_n4096_d128": dict(kind="dense", B=4, Hq=16, Hkv=16, Nq=4096, Nk=4096, d=128,
                                causal=True, seed=2),
-    "c3_causal_gqa_d128_outliers": dict(kind="dense", B=2, Hq=32, Hkv=8, Nq=8192, Nk=8192,
+    "gqa_causal_b2_hq32_hkv8_n8192_d128_koutliers": dict(kind="dense", B=2, Hq=32, Hkv=8, Nq=8192, Nk=8192,
                                         d=128, causal=True, seed=3, k_outlier_frac=0.01,
                                         k_outlier_scale=3.0),
-    "c4_varlen_chunked_prefill": dict(kind="varlen", n_seqs=16, nk_lo=256, nk_hi=8192,
+    "varlen_chunked_prefill_16seq_hq32_hkv8": dict(kind="varlen", n_seqs=16, nk_lo=256, nk_hi=8192,
                                       q_div=4, Hq=32, Hkv=8, d=128, causal=True, seed=4),
-    "c5_splitkv_paged_decode": dict(kind="decode", B=64, Hq=32, Hkv=8, d=128, nk_lo=4096,
+    "paged_decode_b64_hq32_hkv8_d128": dict(kind="decode", B=64, Hq=32, Hkv=8, d=128, nk_lo=4096,
                                     nk_hi=32768, page=PAGE_SIZE, seed=5),
 }
 
