@@ -12,13 +12,6 @@
 // logical key t of request b is row t % page of physical page
 // block_table[b][t / page].
 //
-// Split kernel: one workgroup per (chunk, K/V head, request).  The chunk is
-// walked in tiles of BC = 32 * NW keys inside one page; each wave owns 32 keys
-// of every tile and keeps its own online-softmax state over them (the query
-// rows are few, so the keys are what gets divided).  At the end the waves'
-// states are merged in LDS, in a fixed order, and the chunk's normalised
-// output and lse are written.
-
 #include "attn_tile.h"
 #include "attn_launch.h"
 
@@ -26,27 +19,63 @@ namespace attn {
 
 constexpr int kPage = 256;
 
-template <int D, int QB, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecodeParams p) {
-    constexpr int NT = NW * 64;
-    constexpr int BC = 32 * NW;
+// Build-time knobs of the split kernel (defaults are the measured best):
+// keep the 8 K/V heads of a (request, chunk) on one XCD, and the waves per
+// SIMD the register budget targets.
+#ifndef ATTN_DEC_XCD_GROUP
+#define ATTN_DEC_XCD_GROUP 0
+#endif
+#ifndef ATTN_DEC_WPE
+#define ATTN_DEC_WPE 1
+#endif
+
+// Split kernel: one wave (one workgroup) per (chunk, K/V head, request).  The
+// chunk is walked in tiles of 32 keys that never straddle a page; K and V of a
+// tile go straight from HBM into LDS (16-byte buffer loads with the lds flag,
+// zeros past the valid rows), V is read back transposed, and NS LDS stages
+// keep NS - 1 tiles in flight while one is computed, so each wave sustains
+// several tens of KiB of outstanding reads without any barrier.
+template <int D, int QB, int NS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ATTN_DEC_WPE)))
+void attn_decode_split_kernel(DecodeParams p) {
+    constexpr int BC = 32;
     constexpr int DB = D / 32;
     constexpr int KS = D / 16;
     static_assert(kPage % BC == 0, "tiles must not straddle pages");
-    using Tile = KVTile<D, BC, NT>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * Tile::BYTES];
-    static_assert(32 * QB * D * 4 + 2 * 32 * QB * 4 <= 2 * Tile::BYTES, "merge buffer");
+    static_assert(NS >= 2 && NS <= 4, "stage count");
+    using Tile = KVDirect<D, BC, 1>;
+    constexpr int LOADS = 2 * Tile::PER_WAVE;  // load instructions per tile
+    static_assert((NS - 1) * LOADS < 64, "outstanding loads must fit vmcnt");
+    // Distinct LDS objects, named statically after unrolling, so that the
+    // compiler never waits for in-flight DMA before reading a resident stage.
+    __shared__ __attribute__((aligned(1024))) char stage0[Tile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage1[Tile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage2[NS > 2 ? Tile::BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) char stage3[NS > 3 ? Tile::BYTES : 16];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x;
     const int l32 = lane & 31;
-    // The K/V heads of one (request, chunk) are consecutive workgroups: their
-    // rows interleave in the same cache pages, so they read those pages at
-    // about the same time.
-    const int kvh = blockIdx.x % p.hkv;
-    const int split = (blockIdx.x / p.hkv) % p.n_splits;
-    const int b = blockIdx.x / (p.hkv * p.n_splits);
+    // The K/V heads of one (request, chunk) read interleaved rows of the same
+    // cache pages, so they run close together in time.  Workgroups are dealt
+    // to the 8 XCDs round-robin; with ATTN_DEC_XCD_GROUP the heads of a
+    // (request, chunk) are also kept on one XCD (one L2).
+    int kvh, unit;
+#if ATTN_DEC_XCD_GROUP
+    if (p.hkv == 8) {
+        const int bid = blockIdx.x;
+        kvh = (bid >> 3) & 7;
+        unit = (bid & 7) | ((bid >> 6) << 3);
+    } else {
+        kvh = blockIdx.x % p.hkv;
+        unit = blockIdx.x / p.hkv;
+    }
+#else
+    kvh = blockIdx.x % p.hkv;
+    unit = blockIdx.x / p.hkv;
+#endif
+    const int split = unit % p.n_splits;
+    const int b = unit / p.n_splits;
+    if (b >= p.batch) return;  // padding of the grouped grid
     const int g = p.hq / p.hkv;
     const int hq0 = kvh * g;
 
@@ -67,6 +96,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecodeParams
     const int n_tiles = key_end > key_begin ? (key_end - key_begin + BC - 1) / BC : 0;
 
     const long row_stride = (long)p.hkv * D;
+    const uint32_t stride_b = (uint32_t)(row_stride * 2);
     const int32_t* table = p.block_table + (long)b * p.max_pages;
 
     // Q^T fragments: rows are the g query heads of this K/V head.
@@ -83,6 +113,11 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecodeParams
         }
     }
 
+    // Q must be in registers before any tile DMA is issued: otherwise the
+    // compiler cannot tell the Q loads from the DMA loads and drains every
+    // outstanding load before each tile's first MFMA.
+    wait_vmem();
+
     f32x16 oacc[DB][QB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -98,168 +133,173 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_split_kernel(DecodeParams
     }
     const float c2 = p.scale * kLog2e;
 
-    // Locate tile t: base row pointers and the number of valid keys.
-    auto locate = [&](int t, const uint16_t*& kb, const uint16_t*& vb, int& nvalid) {
+    // Issue the loads of tile t into stage st (page lookup included).
+    auto issue = [&](int t, char* st) __attribute__((always_inline)) {
         const int key0 = key_begin + t * BC;
         const int phys = table[key0 / kPage];
-        nvalid = min(BC, key_end - key0);
+        int nvalid = min(BC, key_end - key0);
+        const uint16_t* kb = p.k_cache;
+        const uint16_t* vb = p.v_cache;
         if (phys < 0 || phys >= p.num_pages) {
             bad = true;
             nvalid = 0;
-            kb = p.k_cache;
-            vb = p.v_cache;
+        } else {
+            const long row0 = (long)phys * kPage + key0 % kPage;
+            kb = p.k_cache + row0 * row_stride + (long)kvh * D;
+            vb = p.v_cache + row0 * row_stride + (long)kvh * D;
+        }
+        Tile::issue(kb, vb, stride_b, nvalid, lds_addr(st), 0, lane);
+    };
+    // Wait until tile t has landed: the loads of the later tiles already
+    // issued (at most NS - 1 of them) may stay in flight.
+    auto wait_tile = [&](int t) __attribute__((always_inline)) {
+        const int later = min(NS - 1, n_tiles - 1 - t);
+        if (later >= NS - 1) {
+            wait_vmem_le<(NS - 1) * LOADS>();
             return;
         }
-        const long row0 = (long)phys * kPage + key0 % kPage;
-        kb = p.k_cache + row0 * row_stride + (long)kvh * D;
-        vb = p.v_cache + row0 * row_stride + (long)kvh * D;
-    };
-
-    Tile tile;
-    int nvalid_cur = 0, nvalid_next = 0;
-    if (n_tiles > 0) {
-        const uint16_t *kb, *vb;
-        locate(0, kb, vb, nvalid_cur);
-        tile.load(kb, vb, row_stride, nvalid_cur, tid);
-        tile.store(smem, smem + Tile::K_BYTES, tid);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-        char* ks = smem + (t & 1) * Tile::BYTES;
-        char* vs = ks + Tile::K_BYTES;
-        if (t + 1 < n_tiles) {
-            const uint16_t *kb, *vb;
-            locate(t + 1, kb, vb, nvalid_next);
-            tile.load(kb, vb, row_stride, nvalid_next, tid);
+        if constexpr (NS > 3) {
+            if (later == 2) {
+                wait_vmem_le<2 * LOADS>();
+                return;
+            }
         }
-        if (32 * wave < nvalid_cur) {
-            f32x16 sacc[QB];
+        if constexpr (NS > 2) {
+            if (later == 1) {
+                wait_vmem_le<LOADS>();
+                return;
+            }
+        }
+        wait_vmem();
+    };
+    auto compute = [&](int t, const char* st) __attribute__((always_inline)) {
+        const char* ks = st;
+        const char* vs = st + Tile::K_BYTES;
+        const int nvalid = min(BC, key_end - (key_begin + t * BC));
+        // S^T = K Q^T, two interleaved accumulation chains over d.
+        f32x16 sacc[QB], sacc2[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[qb][r] = 0.0f;
+                sacc2[qb][r] = 0.0f;
+            }
+#pragma unroll
+        for (int s = 0; s < KS; s += 2) {
+            const u32x4 a0 = read_k_frag<D>(ks, 0, s, lane);
+            const u32x4 a1 = read_k_frag<D>(ks, 0, s + 1, lane);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                sacc[qb] = mfma32(a0, qf[qb][s], sacc[qb]);
+                sacc2[qb] = mfma32(a1, qf[qb][s + 1], sacc2[qb]);
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb] += sacc2[qb];
+        if (nvalid < BC) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const u32x4 a = read_k_frag<D>(ks, wave, s, lane);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sacc[qb] = mfma32(a, qf[qb][s], sacc[qb]);
-            }
-            if (32 * wave + 32 > nvalid_cur) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (score_key(wave, r, lane) >= nvalid_cur) sacc[qb][r] = -INFINITY;
-            }
-            u32x4 pb[QB][2];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
-                mx = pair_max(mx);
-                const float m_new = mx * c2;
-                const bool raise = m_new > m_run[qb] + kRescaleThreshold;
-                const bool scale_old = raise && (m_run[qb] != -INFINITY);
-                if (__builtin_amdgcn_ballot_w64(scale_old)) {
-                    const float alpha = scale_old ? exp2f(m_run[qb] - m_new) : 1.0f;
-                    l_part[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
-                }
-                if (raise) m_run[qb] = m_new;
-                const float shift = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-                float rs = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c2, -shift));
-                    sacc[qb][r] = e;
-                    rs += e;
-                }
-                l_part[qb] += rs;
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    u32x4 w;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        w[j] = pack_bf16x2(sacc[qb][8 * c + 2 * j], sacc[qb][8 * c + 2 * j + 1]);
-                    pb[qb][c] = w;
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const u32x4 a = read_vt_frag<BC>(vs, db, wave, c, lane);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(a, pb[qb][c], oacc[db][qb]);
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (score_key(0, r, lane) >= nvalid) sacc[qb][r] = -INFINITY;
         }
-        if (t + 1 < n_tiles) {
-            char* nks = smem + ((t + 1) & 1) * Tile::BYTES;
-            tile.store(nks, nks + Tile::K_BYTES, tid);
+        u32x4 pb[QB][2];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
+            mx = pair_max(mx);
+            const float m_new = mx * c2;
+            const bool raise = m_new > m_run[qb] + kRescaleThreshold;
+            const bool scale_old = raise && (m_run[qb] != -INFINITY);
+            if (__builtin_amdgcn_ballot_w64(scale_old)) {
+                const float alpha = scale_old ? exp2f(m_run[qb] - m_new) : 1.0f;
+                l_part[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
+            }
+            if (raise) m_run[qb] = m_new;
+            const float shift = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+            float rs = 0.0f;
+            float e[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c2, -shift));
+                rs += e[r];
+            }
+            l_part[qb] += rs;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(e[8 * c + 2 * j], e[8 * c + 2 * j + 1]);
+                pb[qb][c] = w;
+            }
         }
-        nvalid_cur = nvalid_next;
-        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x4 a = read_vt_frag_tr<D>(vs, db, 0, c, lane);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(a, pb[qb][c], oacc[db][qb]);
+            }
+    };
+
+    // Tile t lives in stage t % NS.  Step t first refills the stage that held
+    // tile t - 1 (finished in the previous step) with tile t + NS - 1.
+    auto step = [&](int t, const char* cur, char* refill) __attribute__((always_inline)) {
+        if (t + NS - 1 < n_tiles) issue(t + NS - 1, refill);
+        wait_tile(t);
+        compute(t, cur);
+    };
+    if (n_tiles > 0) issue(0, stage0);
+    if (NS > 2 && 1 < n_tiles) issue(1, stage1);
+    if (NS > 3 && 2 < n_tiles) issue(2, stage2);
+    for (int t = 0; t < n_tiles; t += NS) {
+        if constexpr (NS == 4) {
+            step(t, stage0, stage3);
+            if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
+            if (t + 2 < n_tiles) step(t + 2, stage2, stage1);
+            if (t + 3 < n_tiles) step(t + 3, stage3, stage2);
+        } else if constexpr (NS == 3) {
+            step(t, stage0, stage2);
+            if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
+            if (t + 2 < n_tiles) step(t + 2, stage2, stage1);
+        } else {
+            step(t, stage0, stage1);
+            if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
+        }
     }
 
-    // ---- merge the waves' states (fixed order, deterministic) ----------------
-    // LDS: mbuf[NW][32*QB] running shifts, then obuf[32*QB][D] and lbuf[32*QB].
-    float* mbuf = reinterpret_cast<float*>(smem);
-    float* obuf = mbuf + NW * 32 * QB;
-    float* lbuf = obuf + 32 * QB * D;
+    // ---- write the normalised partial and its lse ----------------------------
+    const long part_row = ((long)split * p.batch + b) * p.hq + hq0;
     const int h = lane >> 5;
-    if (h == 0) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) mbuf[wave * 32 * QB + 32 * qb + l32] = m_run[qb];
-    }
-    __syncthreads();
-    float wscale[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int j = 32 * qb + l32;
-        float M = -INFINITY;
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, mbuf[w * 32 * QB + j]);
-        wscale[qb] = (m_run[qb] == -INFINITY) ? 0.0f : exp2f(m_run[qb] - M);
-    }
-    for (int w = 0; w < NW; ++w) {
-        if (wave == w) {
+        const float L = pair_sum(l_part[qb]);
+        if (j < g) {
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            float* orow = p.out_part + (part_row + j) * D;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int j = 32 * qb + l32;
-                if (j < g) {
-                    const float lt = pair_sum(l_part[qb]) * wscale[qb];
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                    for (int db = 0; db < DB; ++db)
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 w;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int d = 32 * db + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const float v = oacc[db][qb][r] * wscale[qb];
-                            obuf[j * D + d] = (w == 0) ? v : obuf[j * D + d] + v;
-                        }
-                    if (h == 0) lbuf[j] = (w == 0) ? lt : lbuf[j] + lt;
+                    for (int i = 0; i < 4; ++i) w[i] = bad ? NAN : oacc[db][qb][4 * q4 + i] * inv;
+                    *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4 + 4 * h) = w;
                 }
+            if (h == 0) {
+                float lse = L > 0.0f ? (m_run[qb] + __log2f(L)) * kLn2 : -INFINITY;
+                if (bad) lse = NAN;
+                p.lse_part[part_row + j] = lse;
             }
-        }
-        __syncthreads();
-    }
-    // ---- write the normalised partial and its lse ----------------------------
-    const long part_row = ((long)split * p.batch + b) * p.hq + hq0;
-    for (int i = tid; i < g * D; i += NT) {
-        const int j = i / D, d = i % D;
-        float M = -INFINITY;
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, mbuf[w * 32 * QB + j]);
-        const float L = lbuf[j];
-        float o = L > 0.0f ? obuf[j * D + d] / L : 0.0f;
-        if (bad) o = NAN;
-        p.out_part[(part_row + j) * D + d] = o;
-        if (d == 0) {
-            float lse = L > 0.0f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-            if (bad) lse = NAN;
-            p.lse_part[part_row + j] = lse;
         }
     }
 }
@@ -308,25 +348,26 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(CombineParams p
         p.lse[bh] = poison ? NAN : (L > 0.0f ? M + __logf(L) : -INFINITY);
 }
 
-template <int D, int QB, int NW>
+template <int D, int QB, int NS>
 static hipError_t launch_split_cfg(const DecodeParams& p, hipStream_t s) {
     if (p.n_splits <= 0 || p.batch <= 0) return hipSuccess;
-    const long grid = (long)p.n_splits * p.hkv * p.batch;
+    long grid = (long)p.n_splits * p.hkv * p.batch;
+    if (ATTN_DEC_XCD_GROUP && p.hkv == 8) grid = (grid + 63) / 64 * 64;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_decode_split_kernel<D, QB, NW>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                       s, p);
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, QB, NS>), dim3((unsigned)grid), dim3(64), 0, s, p);
     return hipGetLastError();
 }
 
-#ifndef ATTN_DEC_NW
-#define ATTN_DEC_NW 2
+// LDS stages per wave (tiles in flight + 1).
+#ifndef ATTN_DEC_STAGES
+#define ATTN_DEC_STAGES 3
 #endif
 
 template <int D>
 static hipError_t launch_split_d(const DecodeParams& p, hipStream_t s) {
-    constexpr int NW = D >= 256 ? 2 : ATTN_DEC_NW;
+    constexpr int NS = D >= 256 ? 2 : ATTN_DEC_STAGES;
     const int g = p.hq / p.hkv;
-    return g <= 32 ? launch_split_cfg<D, 1, NW>(p, s) : launch_split_cfg<D, 2, NW>(p, s);
+    return g <= 32 ? launch_split_cfg<D, 1, NS>(p, s) : launch_split_cfg<D, 2, NS>(p, s);
 }
 
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, hipStream_t s) {

@@ -51,7 +51,7 @@ void attn_fwd_kernel(FwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int l32 = lane & 31;
 
     // Work item: heaviest query tiles first; when the (sequence, head) count
@@ -137,7 +137,7 @@ void attn_fwd_kernel(FwdParams p) {
     }
     const float c2 = p.scale * kLog2e;
 
-    if (n_tiles > 0) Tile::issue(kbase, vbase, stride_b, Nk, stage0, wave, lane);
+    if (n_tiles > 0) Tile::issue(kbase, vbase, stride_b, Nk, lds_addr(stage0), wave, lane);
     wait_vmem();
     __syncthreads();
 
@@ -146,7 +146,7 @@ void attn_fwd_kernel(FwdParams p) {
         const char* vs = cur + Tile::K_BYTES;
         if (t + 1 < n_tiles) {
             const long off = (long)(t + 1) * BC * kv_stride;
-            Tile::issue(kbase + off, vbase + off, stride_b, Nk - (t + 1) * BC, nxt, wave, lane);
+            Tile::issue(kbase + off, vbase + off, stride_b, Nk - (t + 1) * BC, lds_addr(nxt), wave, lane);
         }
         const int k0 = t * BC;
         const bool active = wave_rows && (!CAUSAL || k0 <= w_last_key);

@@ -29,6 +29,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -200,17 +201,48 @@ struct KVTile {
 // V[key0 .. key0 + 3][d0 + j]: four consecutive keys of one d column, i.e. half
 // of a V^T A-operand fragment.
 
-using lds_ptr_t = __attribute__((address_space(3))) void*;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
 
 // Wait until every vector memory operation of this wave has completed
 // (s_waitcnt vmcnt(0); exp and lgkm counters left unconstrained).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N vector memory operations of this wave are still
+// outstanding (they complete in issue order).  gfx9 s_waitcnt encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, char* lds_base,
-                                                  uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_ptr_t)(__attribute__((address_space(3))) char*)lds_base, 16, voff, 0, 0, 0);
+// Buffer resource words for [base, base + bytes): 48-bit base, stride 0,
+// num_records = bytes, gfx9 word 3 (32-bit data format, no swizzle).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// One 16-byte-per-lane buffer load straight into LDS: lane i's data lands at
+// LDS byte lds_base + 16 * i (lds_base is wave-uniform and goes to M0).
+// Written as inline assembly so that the compiler does not track these LDS
+// writes: it would otherwise drain every outstanding load before LDS reads it
+// cannot prove unrelated.  Every consumer waits explicitly (wait_vmem*)
+// before reading a stage and synchronises as needed.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds_base, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(rsrc)
+        : "memory", "m0");
 }
 
 // Swizzle for V rows read by ds_read_b64_tr_b16: one instruction touches 8
@@ -237,22 +269,23 @@ struct KVDirect {
     static constexpr int RPI = 1024 / ROWB;        // rows per instruction
     static_assert(INSTR % NW == 0, "each wave issues the same number of loads");
 
-    // Issue this wave's share of the loads of one tile into stage `st`.
-    // kbase/vbase: first row of the tile; consecutive rows `stride_b` bytes
-    // apart; the first `nvalid` rows are real keys.
+    // Issue this wave's share of the loads of one tile into the stage at LDS
+    // byte address `st` (K at st, V at st + K_BYTES).  kbase/vbase: first row
+    // of the tile; consecutive rows `stride_b` bytes apart; the first
+    // `nvalid` rows are real keys.
     __device__ __forceinline__ static void issue(const uint16_t* kbase, const uint16_t* vbase,
-                                                 uint32_t stride_b, int nvalid, char* st,
+                                                 uint32_t stride_b, int nvalid, uint32_t st,
                                                  int wave, int lane) {
         const uint32_t nrec = nvalid > 0 ? (uint32_t)(nvalid < BC ? nvalid : BC) * stride_b : 0u;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nrec);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nrec);
+        const u32x4 rk = rsrc_words(kbase, nrec);
+        const u32x4 rv = rsrc_words(vbase, nrec);
 #pragma unroll
         for (int j = 0; j < PER_WAVE; ++j) {
             const int i = wave * PER_WAVE + j;
             const uint32_t row = i * RPI + lane / CH;
             const uint32_t pc = lane % CH;
-            buffer_load_lds16(rk, st + i * 1024, row * stride_b + ((pc ^ swz<CH>(row)) * 16));
-            buffer_load_lds16(rv, st + K_BYTES + i * 1024, row * stride_b + ((pc ^ swz_tr<CH>(row)) * 16));
+            dma16(rk, st + i * 1024, row * stride_b + ((pc ^ swz<CH>(row)) * 16));
+            dma16(rv, st + K_BYTES + i * 1024, row * stride_b + ((pc ^ swz_tr<CH>(row)) * 16));
         }
     }
 };
