@@ -54,22 +54,44 @@ void attn_fwd_kernel(FwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int l32 = lane & 31;
 
-    // Work item: heaviest query tiles first; when the (sequence, head) count
-    // is a multiple of 8, all query tiles of a head run on the same XCD
-    // (workgroups are dealt to the 8 XCDs round-robin), so that head's K/V
-    // stays in one L2.
+    // Work item: heaviest query tiles first (workgroups are dealt to the 8
+    // XCDs round-robin, and each XCD runs its share in launch order).
     const int BH = p.batch * p.hq;
     const int bid = blockIdx.x;
-    int qt, bh;
-    if ((BH & 7) == 0) {
-        const int hpx = BH >> 3, x = bid & 7, kk = bid >> 3;
-        qt = p.n_qtiles - 1 - kk / hpx;
-        bh = x * hpx + kk % hpx;
+    int qt, b, hq;
+    if constexpr (VARLEN) {
+        // Sequences differ in length, so a block of whole sequences per XCD
+        // would load the XCDs unevenly.  Work items (query tile, sequence)
+        // run in query-tile-descending order and the query heads of each
+        // item are spread over the XCDs: XCD x takes heads
+        // [x*hq/8, (x+1)*hq/8), which also keeps a GQA group on one L2.
+        int item;
+        if ((p.hq & 7) == 0) {
+            const int hpx = p.hq >> 3, x = bid & 7, kk = bid >> 3;
+            item = kk / hpx;
+            hq = x * hpx + kk % hpx;
+        } else {
+            item = bid / p.hq;
+            hq = bid % p.hq;
+        }
+        qt = p.n_qtiles - 1 - item / p.batch;
+        b = item % p.batch;
     } else {
-        qt = p.n_qtiles - 1 - bid / BH;
-        bh = bid % BH;
+        // Equal-length sequences: when the (sequence, head) count is a
+        // multiple of 8, all query tiles of a head run on the same XCD, so
+        // that head's K/V stays in one L2.
+        int bh;
+        if ((BH & 7) == 0) {
+            const int hpx = BH >> 3, x = bid & 7, kk = bid >> 3;
+            qt = p.n_qtiles - 1 - kk / hpx;
+            bh = x * hpx + kk % hpx;
+        } else {
+            qt = p.n_qtiles - 1 - bid / BH;
+            bh = bid % BH;
+        }
+        b = bh / p.hq;
+        hq = bh % p.hq;
     }
-    const int b = bh / p.hq, hq = bh % p.hq;
     const int kvh = hq / (p.hq / p.hkv);
 
     int q_off, k_off, Nq, Nk;
