@@ -337,7 +337,7 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, hip
 #define ATTN_FWD128_CFG 1, 64, 8, 2
 #endif
 #ifndef ATTN_FWD64_CFG
-#define ATTN_FWD64_CFG 2, 64, 4, 1
+#define ATTN_FWD64_CFG 2, 64, 4, 2
 #endif
 #ifndef ATTN_FWD256_CFG
 #define ATTN_FWD256_CFG 1, 32, 4, 1
