@@ -92,6 +92,72 @@ def load_traffic(kernel_key, digest):
     return k.get("hbm_bytes_per_launch")
 
 
+TRAFFIC_KERNELS = {"attn_fwd_kernel": "attn_fwd_kernel", "attn_decode_split_kernel": "attn_decode_split_kernel"}
+
+
+def _counter_rows(path, counter):
+    """(kernel name, value in KiB) per dispatch from a rocprofv3 counter_collection.csv."""
+    import csv
+
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib, commands):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch)
+    of `bench.py --copy-calibration-mib N` into profiles/hbm_traffic.json.
+
+    The calibration copy (a same-dtype tensor copy, which the HIP runtime runs
+    as its copyBuffer blit kernel) reads and writes N MiB exactly once; the
+    ratio of that size to what each counter reports for it scales the counter
+    for the attention kernels.  It is the copyBuffer dispatch with the largest
+    counter value.
+    """
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    expect_kib = copy_mib * 1024.0
+
+    def calib(rows):
+        copies = [v for n, v in rows if "copyBuffer" in n]
+        if not copies:
+            raise SystemExit("no copy kernel in the counter file: run bench.py with --copy-calibration-mib")
+        measured = max(copies)
+        return expect_kib / measured, measured
+
+    fr, fm = calib(fetch)
+    wr, wm = calib(write)
+    kernels = {}
+    for key, pat in TRAFFIC_KERNELS.items():
+        fv = [v for n, v in fetch if pat in n]
+        wv = [v for n, v in write if pat in n]
+        if not fv or not wv:
+            continue
+        f_kib = sum(fv) / len(fv)
+        w_kib = sum(wv) / len(wv)
+        kernels[key] = {
+            "dispatches": [len(fv), len(wv)],
+            "fetch_kib_per_launch": round(f_kib, 1),
+            "write_kib_per_launch": round(w_kib, 1),
+            "hbm_bytes_per_launch": int(round((f_kib * fr + w_kib * wr) * 1024)),
+        }
+    rec = {
+        "source_digest": source_digest(),
+        "commands": commands,
+        "copy_calibration": {"mib": copy_mib, "fetch_kib_measured": fm, "write_kib_measured": wm,
+                             "fetch_scale": round(fr, 4), "write_scale": round(wr, 4)},
+        "kernels": kernels,
+    }
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
     import numpy as np
@@ -149,7 +215,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for counter scaling)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: write profiles/hbm_traffic.json from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a run with "
+                         "--copy-calibration-mib, then exit")
+    ap.add_argument("--traffic-commands", nargs="*", default=[],
+                    help="with --write-traffic: the profiler commands, stored with the figures")
     args = ap.parse_args()
+    if args.write_traffic:
+        if not args.copy_calibration_mib:
+            print("--write-traffic needs the --copy-calibration-mib value of the profiled run",
+                  file=sys.stderr)
+            return 2
+        return write_traffic(args.write_traffic[0], args.write_traffic[1],
+                             args.copy_calibration_mib, args.traffic_commands)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
