@@ -222,11 +222,13 @@ int attn_decode_default_chunk(int batch, int num_heads_kv, int max_seqlen_k, int
     if (batch < 1) batch = 1;
     if (num_heads_kv < 1) num_heads_kv = 1;
     if (max_seqlen_k < 1) return 256;
-    // Aim for about 32 split workgroups per compute unit over the longest
-    // request (measured best for long caches; each split reads at least one
-    // page); keep chunks between one page and 64 pages.
+    // Aim for about 64 split waves (one per K/V head and chunk) per compute
+    // unit over the longest request: eight run at once on a compute unit, and
+    // several rounds of them keep the tail short (measured best for long
+    // caches; each split reads at least one page); keep chunks between one
+    // page and 64 pages.
     const long units = (long)batch * num_heads_kv;
-    const long want = 32L * num_cus;
+    const long want = 64L * num_cus;
     long splits = (want + units - 1) / units;
     if (splits < 1) splits = 1;
     long chunk = ((long)max_seqlen_k + splits - 1) / splits;

@@ -19,63 +19,55 @@ namespace attn {
 
 constexpr int kPage = 256;
 
-// Build-time knobs of the split kernel (defaults are the measured best):
-// keep the 8 K/V heads of a (request, chunk) on one XCD, and the waves per
-// SIMD the register budget targets.
-#ifndef ATTN_DEC_XCD_GROUP
-#define ATTN_DEC_XCD_GROUP 0
-#endif
-#ifndef ATTN_DEC_WPE
-#define ATTN_DEC_WPE 1
-#endif
+// Waves per SIMD the split kernel's register budget targets: two when the
+// query heads of a K/V head fit one 16-column block and d <= 128.
+template <int D, int QB>
+constexpr int dec_wpe() { return (QB == 1 && D <= 128) ? 2 : 1; }
 
-// Split kernel: one wave (one workgroup) per (chunk, K/V head, request).  The
-// chunk is walked in tiles of 32 keys that never straddle a page; K and V of a
-// tile go straight from HBM into LDS (16-byte buffer loads with the lds flag,
-// zeros past the valid rows), V is read back transposed, and NS LDS stages
-// keep NS - 1 tiles in flight while one is computed, so each wave sustains
-// several tens of KiB of outstanding reads without any barrier.
-template <int D, int QB, int NS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ATTN_DEC_WPE)))
+// Tiles held in registers (in flight) per wave: two unless that would spill.
+template <int D, int QB>
+constexpr int dec_sets() { return (D <= 128 && D * QB <= 256) ? 2 : 1; }
+
+// Split kernel: one wave per (K/V head, chunk, request); the HPW waves of a
+// workgroup take HPW adjacent K/V heads of the same (request, chunk), so the
+// interleaved head segments of each cache row are read from one compute unit
+// at about the same time (measured: 5-10% more HBM throughput than one head
+// per workgroup).  The chunk is walked in tiles of 32 keys that never
+// straddle a page.  S^T = K Q^T and O^T = V^T P^T run on 16x16x32 MFMAs (the g
+// query heads of the K/V head are the columns, so a 16-column block wastes
+// least when g is small).  K and V rows come into registers with coalesced
+// 16-byte loads (each 64-lane load covers whole row segments) and are written
+// to this wave's LDS region, from where the A operands are read (K directly,
+// V^T with transposed reads).  NR register sets (two where the registers
+// allow) hold tiles t .. t+NR-1 while tile t is computed, and tile t+NR is
+// issued into tile t's set as soon as it has been written to LDS, so every
+// wave keeps up to NR tiles (16 KiB each at d = 128) of reads in flight with
+// no barrier.  A wave's LDS accesses execute in program order, so one LDS
+// region per wave suffices: tile t+1's rows land after tile t's reads.
+template <int D, int QB, int HPW>
+__global__ __launch_bounds__(64 * HPW) __attribute__((amdgpu_waves_per_eu(dec_wpe<D, QB>(), dec_wpe<D, QB>())))
 void attn_decode_split_kernel(DecodeParams p) {
-    constexpr int BC = 32;
-    constexpr int DB = D / 32;
-    constexpr int KS = D / 16;
+    constexpr int BC = 32;            // keys per tile: two 16-key blocks
+    constexpr int KD = D / 32;        // 32-wide d steps of S^T
+    constexpr int DB = D / 16;        // 16-wide d blocks of O^T
+    constexpr int CH = D / 8;         // 16-byte chunks per cache row
+    constexpr int RPI = 64 / CH;      // rows per 64-lane 16-byte load
+    constexpr int VI = BC / RPI;      // V loads per tile
+    constexpr uint32_t VBYTES = BC * D * 2;
     static_assert(kPage % BC == 0, "tiles must not straddle pages");
-    static_assert(NS >= 2 && NS <= 4, "stage count");
-    using Tile = KVDirect<D, BC, 1>;
-    constexpr int LOADS = 2 * Tile::PER_WAVE;  // load instructions per tile
-    static_assert((NS - 1) * LOADS < 64, "outstanding loads must fit vmcnt");
-    // Distinct LDS objects, named statically after unrolling, so that the
-    // compiler never waits for in-flight DMA before reading a resident stage.
-    __shared__ __attribute__((aligned(1024))) char stage0[Tile::BYTES];
-    __shared__ __attribute__((aligned(1024))) char stage1[Tile::BYTES];
-    __shared__ __attribute__((aligned(1024))) char stage2[NS > 2 ? Tile::BYTES : 16];
-    __shared__ __attribute__((aligned(1024))) char stage3[NS > 3 ? Tile::BYTES : 16];
+    constexpr int NR = dec_sets<D, QB>();
+    __shared__ __attribute__((aligned(1024))) char smem[HPW * 2 * VBYTES];
 
-    const int lane = threadIdx.x;
-    const int l32 = lane & 31;
-    // The K/V heads of one (request, chunk) read interleaved rows of the same
-    // cache pages, so they run close together in time.  Workgroups are dealt
-    // to the 8 XCDs round-robin; with ATTN_DEC_XCD_GROUP the heads of a
-    // (request, chunk) are also kept on one XCD (one L2).
-    int kvh, unit;
-#if ATTN_DEC_XCD_GROUP
-    if (p.hkv == 8) {
-        const int bid = blockIdx.x;
-        kvh = (bid >> 3) & 7;
-        unit = (bid & 7) | ((bid >> 6) << 3);
-    } else {
-        kvh = blockIdx.x % p.hkv;
-        unit = blockIdx.x / p.hkv;
-    }
-#else
-    kvh = blockIdx.x % p.hkv;
-    unit = blockIdx.x / p.hkv;
-#endif
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, G = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    char* const ksm = smem + wave * (2 * VBYTES);  // this wave's K tile, then V tile
+    char* const vsm = ksm + VBYTES;
+    const int groups = p.hkv / HPW;
+    const int kvh = (blockIdx.x % groups) * HPW + wave;
+    const int unit = blockIdx.x / groups;
     const int split = unit % p.n_splits;
     const int b = unit / p.n_splits;
-    if (b >= p.batch) return;  // padding of the grouped grid
     const int g = p.hq / p.hkv;
     const int hq0 = kvh * g;
 
@@ -99,32 +91,26 @@ void attn_decode_split_kernel(DecodeParams p) {
     const uint32_t stride_b = (uint32_t)(row_stride * 2);
     const int32_t* table = p.block_table + (long)b * p.max_pages;
 
-    // Q^T fragments: rows are the g query heads of this K/V head.
-    u32x4 qf[QB][KS];
+    // Q^T fragments (B operand): column j of block qb is query head
+    // hq0 + 16 qb + j; lane l holds its d values 32 s + 8 (l / 16) .. + 7.
+    u32x4 qf[QB][KD];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int j = 32 * qb + l32;
+        const int j = 16 * qb + l16;
         const uint16_t* qrow = p.q + ((long)b * p.hq + hq0 + j) * D;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KD; ++s) {
             u32x4 z = {0u, 0u, 0u, 0u};
-            if (j < g) z = load16(qrow + (2 * s + (lane >> 5)) * 8);
+            if (j < g) z = load16(qrow + 32 * s + 8 * G);
             qf[qb][s] = z;
         }
     }
 
-    // Q must be in registers before any tile DMA is issued: otherwise the
-    // compiler cannot tell the Q loads from the DMA loads and drains every
-    // outstanding load before each tile's first MFMA.
-    wait_vmem();
-
-    f32x16 oacc[DB][QB];
+    f32x4 oacc[DB][QB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.0f;
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run[QB], l_part[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -133,8 +119,14 @@ void attn_decode_split_kernel(DecodeParams p) {
     }
     const float c2 = p.scale * kLog2e;
 
-    // Issue the loads of tile t into stage st (page lookup included).
-    auto issue = [&](int t, char* st) __attribute__((always_inline)) {
+    // One tile in registers: k[i] and v[i] hold rows RPI i + l / CH, 16-byte
+    // chunk l % CH.  Rows past the valid keys, and every row of a tile whose
+    // page id is out of range, load as zeros.
+    struct Regs {
+        u32x4 k[VI];
+        u32x4 v[VI];
+    };
+    auto load = [&](int t, Regs& R) __attribute__((always_inline)) {
         const int key0 = key_begin + t * BC;
         const int phys = table[key0 / kPage];
         int nvalid = min(BC, key_end - key0);
@@ -148,69 +140,69 @@ void attn_decode_split_kernel(DecodeParams p) {
             kb = p.k_cache + row0 * row_stride + (long)kvh * D;
             vb = p.v_cache + row0 * row_stride + (long)kvh * D;
         }
-        Tile::issue(kb, vb, stride_b, nvalid, lds_addr(st), 0, lane);
+        const uint32_t nrec = (uint32_t)nvalid * stride_b;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, nrec);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, nrec);
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            const uint32_t off = (uint32_t)(RPI * i + lane / CH) * stride_b + (lane % CH) * 16;
+            R.k[i] = buffer_load16(rk, off);
+            R.v[i] = buffer_load16(rv, off);
+        }
     };
-    // Wait until tile t has landed: the loads of the later tiles already
-    // issued (at most NS - 1 of them) may stay in flight.
-    auto wait_tile = [&](int t) __attribute__((always_inline)) {
-        const int later = min(NS - 1, n_tiles - 1 - t);
-        if (later >= NS - 1) {
-            wait_vmem_le<(NS - 1) * LOADS>();
-            return;
-        }
-        if constexpr (NS > 3) {
-            if (later == 2) {
-                wait_vmem_le<2 * LOADS>();
-                return;
-            }
-        }
-        if constexpr (NS > 2) {
-            if (later == 1) {
-                wait_vmem_le<LOADS>();
-                return;
-            }
-        }
-        wait_vmem();
+    // Row-major tile in LDS; 16-byte chunk c of row r sits in slot
+    // c ^ swz_v16(r), so both the 16-row K fragment reads and the transposed
+    // V reads spread over all bank groups.
+    auto slot = [&](uint32_t row, uint32_t c) __attribute__((always_inline)) {
+        return row * (2 * D) + ((c ^ swz_v16<CH>(row)) * 16);
     };
-    auto compute = [&](int t, const char* st) __attribute__((always_inline)) {
-        const char* ks = st;
-        const char* vs = st + Tile::K_BYTES;
+
+    // Compute tile t from R; refill R with tile t + NR once it is in LDS.
+    auto step = [&](int t, Regs& R) __attribute__((always_inline)) {
         const int nvalid = min(BC, key_end - (key_begin + t * BC));
-        // S^T = K Q^T, two interleaved accumulation chains over d.
-        f32x16 sacc[QB], sacc2[QB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[qb][r] = 0.0f;
-                sacc2[qb][r] = 0.0f;
-            }
-#pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            const u32x4 a0 = read_k_frag<D>(ks, 0, s, lane);
-            const u32x4 a1 = read_k_frag<D>(ks, 0, s + 1, lane);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                sacc[qb] = mfma32(a0, qf[qb][s], sacc[qb]);
-                sacc2[qb] = mfma32(a1, qf[qb][s + 1], sacc2[qb]);
-            }
+        for (int i = 0; i < VI; ++i) {
+            const uint32_t row = RPI * i + lane / CH, c = lane % CH;
+            *reinterpret_cast<u32x4*>(ksm + slot(row, c)) = R.k[i];
+            *reinterpret_cast<u32x4*>(vsm + slot(row, c)) = R.v[i];
         }
+        if (t + NR < n_tiles) load(t + NR, R);
+        // ---- S^T = K Q^T: two 16-key blocks --------------------------------
+        // A operand of key block h, d step s: lane l reads key 16 h + l % 16,
+        // d 32 s + 8 (l / 16) .. + 7 (chunk 4 s + l / 16).
+        f32x4 sacc[2][QB];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb] += sacc2[qb];
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[h][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KD; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(ksm + slot(16 * h + l16, 4 * s + G));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sacc[h][qb] = mfma16(a, qf[qb][s], sacc[h][qb]);
+            }
+        // ---- mask the keys past the end of the chunk -------------------------
         if (nvalid < BC) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (score_key(0, r, lane) >= nvalid) sacc[qb][r] = -INFINITY;
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * h + 4 * G + r >= nvalid) sacc[h][qb][r] = -INFINITY;
         }
-        u32x4 pb[QB][2];
+        // ---- online softmax ------------------------------------------------
+        u32x4 pb[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
-            mx = pair_max(mx);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[h][qb][r]);
+            mx = quad_max(mx);
             const float m_new = mx * c2;
             const bool raise = m_new > m_run[qb] + kRescaleThreshold;
             const bool scale_old = raise && (m_run[qb] != -INFINITY);
@@ -218,84 +210,63 @@ void attn_decode_split_kernel(DecodeParams p) {
                 const float alpha = scale_old ? exp2f(m_run[qb] - m_new) : 1.0f;
                 l_part[qb] *= alpha;
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
+                for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
             }
             if (raise) m_run[qb] = m_new;
             const float shift = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
+            float e[2][4];
             float rs = 0.0f;
-            float e[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][r], c2, -shift));
-                rs += e[r];
-            }
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    e[h][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[h][qb][r], c2, -shift));
+                    rs += e[h][r];
+                }
             l_part[qb] += rs;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 w;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(e[8 * c + 2 * j], e[8 * c + 2 * j + 1]);
-                pb[qb][c] = w;
-            }
+            pb[qb] = u32x4{pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]),
+                           pack_bf16x2(e[1][0], e[1][1]), pack_bf16x2(e[1][2], e[1][3])};
         }
+        // ---- O^T += V^T P^T ------------------------------------------------
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int db = 0; db < DB; ++db) {
+            const u32x4 a = read_vt16_tr<D>(vsm, db, lane);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x4 a = read_vt_frag_tr<D>(vs, db, 0, c, lane);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(a, pb[qb][c], oacc[db][qb]);
-            }
+            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma16(a, pb[qb], oacc[db][qb]);
+        }
     };
 
-    // Tile t lives in stage t % NS.  Step t first refills the stage that held
-    // tile t - 1 (finished in the previous step) with tile t + NS - 1.
-    auto step = [&](int t, const char* cur, char* refill) __attribute__((always_inline)) {
-        if (t + NS - 1 < n_tiles) issue(t + NS - 1, refill);
-        wait_tile(t);
-        compute(t, cur);
-    };
-    if (n_tiles > 0) issue(0, stage0);
-    if (NS > 2 && 1 < n_tiles) issue(1, stage1);
-    if (NS > 3 && 2 < n_tiles) issue(2, stage2);
-    for (int t = 0; t < n_tiles; t += NS) {
-        if constexpr (NS == 4) {
-            step(t, stage0, stage3);
-            if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
-            if (t + 2 < n_tiles) step(t + 2, stage2, stage1);
-            if (t + 3 < n_tiles) step(t + 3, stage3, stage2);
-        } else if constexpr (NS == 3) {
-            step(t, stage0, stage2);
-            if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
-            if (t + 2 < n_tiles) step(t + 2, stage2, stage1);
-        } else {
-            step(t, stage0, stage1);
-            if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
+    if constexpr (NR == 2) {
+        Regs r0, r1;
+        if (n_tiles > 0) load(0, r0);
+        if (n_tiles > 1) load(1, r1);
+        for (int t = 0; t < n_tiles; t += 2) {
+            step(t, r0);
+            if (t + 1 < n_tiles) step(t + 1, r1);
         }
+    } else {
+        Regs r0;
+        if (n_tiles > 0) load(0, r0);
+        for (int t = 0; t < n_tiles; ++t) step(t, r0);
     }
 
     // ---- write the normalised partial and its lse ----------------------------
     const long part_row = ((long)split * p.batch + b) * p.hq + hq0;
-    const int h = lane >> 5;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int j = 32 * qb + l32;
-        const float L = pair_sum(l_part[qb]);
+        const int j = 16 * qb + l16;
+        const float L = quad_sum(l_part[qb]);
         if (j < g) {
             const float inv = L > 0.0f ? 1.0f / L : 0.0f;
             float* orow = p.out_part + (part_row + j) * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db) {
+                f32x4 w;
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    f32x4 w;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = bad ? NAN : oacc[db][qb][4 * q4 + i] * inv;
-                    *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * q4 + 4 * h) = w;
-                }
-            if (h == 0) {
+                for (int r = 0; r < 4; ++r) w[r] = bad ? NAN : oacc[db][qb][r] * inv;
+                *reinterpret_cast<f32x4*>(orow + 16 * db + 4 * G) = w;
+            }
+            if (G == 0) {
                 float lse = L > 0.0f ? (m_run[qb] + __log2f(L)) * kLn2 : -INFINITY;
                 if (bad) lse = NAN;
                 p.lse_part[part_row + j] = lse;
@@ -304,36 +275,65 @@ void attn_decode_split_kernel(DecodeParams p) {
     }
 }
 
-// One workgroup (one wave) per (request, query head).
+// Sum and max over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// One workgroup (one wave) per (request, query head).  Lane c holds the lse
+// of split c (64 splits at a time), so the maximum and the weights come from
+// one load per lane and a cross-lane reduction; the partial rows are then
+// summed with the weight of split j broadcast from lane j, several row loads
+// in flight at once.
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(CombineParams p) {
     constexpr int PER = D / 64;
     const int bh = blockIdx.x;
     const int b = bh / p.hq;
     const int lane = threadIdx.x;
-    int Nk = p.seqlens[b];
+    const int Nk = p.seqlens[b];
     const int n = Nk > 0 ? (Nk + p.chunk - 1) / p.chunk : 0;
     const bool bad = Nk < 0 || n > p.n_splits;
+    const long split_stride = (long)p.batch * p.hq;  // rows between splits
+    float M = -INFINITY;
+    bool nan_seen = false;
+    if (!bad) {
+        for (int c0 = 0; c0 < n; c0 += 64) {
+            const int c = c0 + lane;
+            const float x = c < n ? p.lse_part[c * split_stride + bh] : -INFINITY;
+            nan_seen |= (x != x);
+            M = fmaxf(M, x);
+        }
+    }
+    M = wave_max(M);
+    nan_seen = __builtin_amdgcn_ballot_w64(nan_seen) != 0;
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
-    float M = -INFINITY;
-    bool nan_seen = false;
-    for (int c = 0; c < n && !bad; ++c) {
-        const float x = p.lse_part[((long)c * p.batch) * p.hq + bh];
-        nan_seen |= (x != x);
-        M = fmaxf(M, x);
-    }
     float L = 0.0f;
-    if (!bad && M != -INFINITY) {
-        for (int c = 0; c < n; ++c) {
-            const long row = ((long)c * p.batch) * p.hq + bh;
-            const float x = p.lse_part[row];
-            const float w = __expf(x - M);
+    if (!bad && !nan_seen && M != -INFINITY) {
+        for (int c0 = 0; c0 < n; c0 += 64) {
+            const int c = c0 + lane;
+            const float w = c < n ? __expf(p.lse_part[c * split_stride + bh] - M) : 0.0f;
             L += w;
+            const int cnt = min(64, n - c0);
+            const float* rows = p.out_part + ((long)c0 * split_stride + bh) * D + lane;
+#pragma unroll 8
+            for (int j = 0; j < cnt; ++j) {
+                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] += w * p.out_part[row * D + lane + 64 * i];
+                for (int i = 0; i < PER; ++i) acc[i] += wj * rows[(long)j * split_stride * D + 64 * i];
+            }
         }
+        L = wave_sum(L);
     }
     const bool poison = bad || nan_seen;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -348,26 +348,29 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(CombineParams p
         p.lse[bh] = poison ? NAN : (L > 0.0f ? M + __logf(L) : -INFINITY);
 }
 
-template <int D, int QB, int NS>
-static hipError_t launch_split_cfg(const DecodeParams& p, hipStream_t s) {
-    if (p.n_splits <= 0 || p.batch <= 0) return hipSuccess;
-    long grid = (long)p.n_splits * p.hkv * p.batch;
-    if (ATTN_DEC_XCD_GROUP && p.hkv == 8) grid = (grid + 63) / 64 * 64;
+template <int D, int QB, int HPW>
+static hipError_t launch_split_hpw(const DecodeParams& p, hipStream_t s) {
+    const long grid = (long)p.n_splits * (p.hkv / HPW) * p.batch;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_decode_split_kernel<D, QB, NS>), dim3((unsigned)grid), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((attn_decode_split_kernel<D, QB, HPW>), dim3((unsigned)grid), dim3(64 * HPW), 0, s,
+                       p);
     return hipGetLastError();
 }
 
-// LDS stages per wave (tiles in flight + 1).
-#ifndef ATTN_DEC_STAGES
-#define ATTN_DEC_STAGES 3
-#endif
+// Two K/V heads per workgroup when the head count allows it.
+template <int D, int QB>
+static hipError_t launch_split_cfg(const DecodeParams& p, hipStream_t s) {
+    if (p.n_splits <= 0 || p.batch <= 0) return hipSuccess;
+    return (p.hkv % 2 == 0) ? launch_split_hpw<D, QB, 2>(p, s) : launch_split_hpw<D, QB, 1>(p, s);
+}
 
+// 16-column blocks of query heads per K/V head.
 template <int D>
 static hipError_t launch_split_d(const DecodeParams& p, hipStream_t s) {
-    constexpr int NS = D >= 256 ? 2 : ATTN_DEC_STAGES;
     const int g = p.hq / p.hkv;
-    return g <= 32 ? launch_split_cfg<D, 1, NS>(p, s) : launch_split_cfg<D, 2, NS>(p, s);
+    if (g <= 16) return launch_split_cfg<D, 1>(p, s);
+    if (g <= 32) return launch_split_cfg<D, 2>(p, s);
+    return launch_split_cfg<D, 4>(p, s);
 }
 
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, hipStream_t s) {

@@ -328,4 +328,63 @@ __device__ __forceinline__ int score_key(int kb, int r, int lane) {
     return 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// ---- 16x16x32 matrix-core tiles (one-query decode) -------------------------
+// v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8 * (l / 16) + 0..7] and
+// B[8 * (l / 16) + 0..7][l % 16]; result register r of lane l is
+// D[4 * (l / 16) + r][l % 16].
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes that hold
+// one column of a 16x16 result).  v_permlane16_swap with both operands = x
+// leaves each lane holding {x[l], x[l ^ 16]}.
+__device__ __forceinline__ float quad_max(float x) {
+    x = pair_max(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+    x = pair_sum(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Chunk swizzle of a row-major V tile that is read back with 16-lane
+// transposed reads of 16 consecutive rows: 16-byte chunk c of row `row` sits
+// in slot c ^ swz_v16<CH>(row), which puts those 16 rows' segments of one
+// chunk on 16 different bank groups.
+template <int CH>
+__device__ __forceinline__ uint32_t swz_v16(uint32_t row) {
+    if constexpr (CH == 8) {
+        return (row >> 1) & 7u;  // 128-byte rows: odd rows already sit on the other 32 banks
+    } else {
+        static_assert(CH >= 16, "row too short");
+        return row & 15u;
+    }
+}
+
+// A operand of O^T = V^T P^T (16x16x32 shape) for d block db (16 rows of V^T)
+// from a 32-key row-major V tile stored with swz_v16.  Contraction index
+// 8 * (l / 16) + j maps to key 4 * (l / 16) + j for j < 4 and to key
+// 16 + 4 * (l / 16) + (j - 4) for j >= 4: the keys a lane holds in the two
+// 16-key blocks of S^T (result registers 0..3 of each block).
+template <int D>
+__device__ __forceinline__ u32x4 read_vt16_tr(const char* vs, int db, int lane) {
+    constexpr int CH = D / 8;
+    const uint32_t G = lane >> 4, s = lane & 15;
+    const uint32_t d = 16 * db + 4 * (s & 3);
+    const uint32_t k1 = 4 * G + (s >> 2);
+    const uint32_t k2 = k1 + 16;
+    const uint32_t a1 = k1 * (2 * D) + (((d >> 3) ^ swz_v16<CH>(k1)) * 16) + (d & 7) * 2;
+    const uint32_t a2 = k2 * (2 * D) + (((d >> 3) ^ swz_v16<CH>(k2)) * 16) + (d & 7) * 2;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)(vs + a1));
+    const s16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)(vs + a2));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, r1), w2 = __builtin_bit_cast(u32x2, r2);
+    return u32x4{w1[0], w1[1], w2[0], w2[1]};
+}
+
 }  // namespace attn
