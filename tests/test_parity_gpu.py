@@ -235,6 +235,15 @@ def test_decode_mqa_and_wide_groups():
     decode_parity(W.decode_case(lens, 32, 1, 128, seed=61), 512)   # g = 32
     decode_parity(W.decode_case(lens, 64, 1, 128, seed=62), 512)   # g = 64
     decode_parity(W.decode_case(lens, 4, 4, 128, seed=63), 256)    # MHA, g = 1
+    decode_parity(W.decode_case(lens, 16, 1, 128, seed=64), 1024)  # g = 16: one full column block
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(12, 3, 64), (9, 3, 128), (24, 1, 256), (64, 1, 64), (40, 5, 256)],
+                         ids=lambda x: str(x))
+def test_decode_odd_head_counts_and_groups(hq, hkv, d):
+    """Odd K/V head counts (one head per workgroup) and wide groups at every d."""
+    lens = [300, 1, 2049, 4096]
+    decode_parity(W.decode_case(lens, hq, hkv, d, seed=80 + hq + d, poison=True), 1024)
 
 
 def test_config_decode_full_sampled():
