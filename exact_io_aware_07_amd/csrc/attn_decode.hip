@@ -66,8 +66,11 @@ void attn_decode_split_kernel(DecodeParams p) {
     const int groups = p.hkv / HPW;
     const int kvh = (blockIdx.x % groups) * HPW + wave;
     const int unit = blockIdx.x / groups;
-    const int split = unit % p.n_splits;
-    const int b = unit / p.n_splits;
+    // Highest split index first: the last (often partial) chunks of the
+    // requests, and every chunk of the short requests, come at the end of
+    // the grid, where they fill the tail.
+    const int split = p.n_splits - 1 - unit / p.batch;
+    const int b = unit % p.batch;
     const int g = p.hq / p.hkv;
     const int hq0 = kvh * g;
 
@@ -288,49 +291,66 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// One workgroup (one wave) per (request, query head).  Lane c holds the lse
-// of split c (64 splits at a time), so the maximum and the weights come from
-// one load per lane and a cross-lane reduction; the partial rows are then
-// summed with the weight of split j broadcast from lane j, several row loads
-// in flight at once.
+// One workgroup (one wave) per (request, query head).  The partial rows of the
+// first splits are requested before the lse reduction, so the row loads and
+// the max/sum run side by side; weights of split j come from lane j.
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(CombineParams p) {
     constexpr int PER = D / 64;
+    constexpr int RB = 16;  // partial rows in flight
     const int bh = blockIdx.x;
     const int b = bh / p.hq;
     const int lane = threadIdx.x;
     const int Nk = p.seqlens[b];
     const int n = Nk > 0 ? (Nk + p.chunk - 1) / p.chunk : 0;
     const bool bad = Nk < 0 || n > p.n_splits;
-    const long split_stride = (long)p.batch * p.hq;  // rows between splits
-    float M = -INFINITY;
-    bool nan_seen = false;
-    if (!bad) {
-        for (int c0 = 0; c0 < n; c0 += 64) {
-            const int c = c0 + lane;
-            const float x = c < n ? p.lse_part[c * split_stride + bh] : -INFINITY;
-            nan_seen |= (x != x);
-            M = fmaxf(M, x);
-        }
-    }
-    M = wave_max(M);
-    nan_seen = __builtin_amdgcn_ballot_w64(nan_seen) != 0;
+    const long split_stride = (long)p.batch * p.hq;
+    const int nn = bad ? 0 : n;
+    const float* rows = p.out_part + (long)bh * D + lane;
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.0f;
+    // first batch of rows
+    float v[RB][PER];
+#pragma unroll
+    for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[j][i] = j < nn ? rows[(long)j * split_stride * D + 64 * i] : 0.0f;
+    float x = lane < nn ? p.lse_part[lane * split_stride + bh] : -INFINITY;
+    float M = x;
+    bool nan_seen = (x != x);
+    for (int c = lane + 64; c < nn; c += 64) {
+        const float y = p.lse_part[c * split_stride + bh];
+        nan_seen |= (y != y);
+        M = fmaxf(M, y);
+    }
+    M = wave_max(M);
+    nan_seen = __builtin_amdgcn_ballot_w64(nan_seen) != 0;
     float L = 0.0f;
     if (!bad && !nan_seen && M != -INFINITY) {
-        for (int c0 = 0; c0 < n; c0 += 64) {
-            const int c = c0 + lane;
-            const float w = c < n ? __expf(p.lse_part[c * split_stride + bh] - M) : 0.0f;
-            L += w;
-            const int cnt = min(64, n - c0);
-            const float* rows = p.out_part + ((long)c0 * split_stride + bh) * D + lane;
-#pragma unroll 8
-            for (int j = 0; j < cnt; ++j) {
-                const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+        float w = lane < nn ? __expf(x - M) : 0.0f;
+        L = w;
+        for (int c0 = 0; c0 < nn; c0 += 64) {
+            if (c0 > 0) {
+                const int c = c0 + lane;
+                w = c < nn ? __expf(p.lse_part[c * split_stride + bh] - M) : 0.0f;
+                L += w;
+            }
+            const int cnt = min(64, nn - c0);
+            for (int j0 = 0; j0 < cnt; j0 += RB) {
+                if (c0 > 0 || j0 > 0) {
 #pragma unroll
-                for (int i = 0; i < PER; ++i) acc[i] += wj * rows[(long)j * split_stride * D + 64 * i];
+                    for (int j = 0; j < RB; ++j)
+#pragma unroll
+                        for (int i = 0; i < PER; ++i)
+                            v[j][i] = j0 + j < cnt ? rows[(long)(c0 + j0 + j) * split_stride * D + 64 * i] : 0.0f;
+                }
+#pragma unroll
+                for (int j = 0; j < RB; ++j) {
+                    const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j0 + j));
+#pragma unroll
+                    for (int i = 0; i < PER; ++i) acc[i] += wj * v[j][i];
+                }
             }
         }
         L = wave_sum(L);
