@@ -8,6 +8,7 @@ with NumPy, one (sequence, query head) at a time.
 Sources (page title, section):
   * "Deep Dive - FlashAttention": "Exact attention without an n x n workspace",
     "Two tiles by hand", "The public interface is several kernels",
+    "Backward recomputes tiles on purpose" (the gradients),
     "Causal 2.1 is the decode gotcha", "Paged KV is a lookup, not a cache manager".
   * "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)":
     "Runnable Example: Measuring the IO Gap", "Decode-Time Kernels".
@@ -26,4 +27,5 @@ from .attention import (  # noqa: F401
     attention_rows,
     paged_gather,
     decode_ref,
+    attention_bwd_ref,
 )

@@ -211,7 +211,88 @@ def decode_ref(q, k_cache, v_cache, block_table, seqlens_k, *, softmax_scale, re
     return out, lse
 
 
+def _attend_rows_bwd(Q, K, V, G, scale, keep):
+    """Gradients for a block of query rows against one key/value head.
+
+    Q [n, d], K [m, d], V [m, dv], G = dL/d(out) [n, dv] float64; keep
+    [n, m] bool or None.  Returns dQ [n, d], and this block's contribution to
+    dK [m, d] and dV [m, dv].
+
+    "Deep Dive - FlashAttention", "Backward recomputes tiles on purpose": with
+    S = scale * Q K^T and P = softmax(S) row by row, dV = P^T G, dP = G V^T,
+    and dS = P * (dP - rowsum(P * dP)) (the softmax Jacobian applied row by
+    row; the row sum is broadcast over keys).  Masked probabilities, and with
+    them their gradients, are zero; a row with no allowed key has P = 0 and
+    contributes nothing.  The chain rule through S = scale * Q K^T gives
+    dQ = scale * dS K and dK = scale * dS^T Q.
+    """
+    n, m = Q.shape[0], K.shape[0]
+    if m == 0:
+        return np.zeros_like(Q), np.zeros_like(K), np.zeros((0, V.shape[1]))
+    S = scale * (Q @ K.T)
+    if keep is not None:
+        S = np.where(keep, S, -np.inf)
+    row_max = S.max(axis=1)
+    nonempty = np.isfinite(row_max)
+    E = np.exp(S - np.where(nonempty, row_max, 0.0)[:, None])
+    P = E / np.where(nonempty, E.sum(axis=1), 1.0)[:, None]
+    P[~nonempty] = 0.0
+    dV = P.T @ G
+    dP = G @ V.T
+    D = (P * dP).sum(axis=1)
+    dS = P * (dP - D[:, None])
+    dQ = scale * (dS @ K)
+    dK = scale * (dS.T @ Q)
+    return dQ, dK, dV
+
+
+def attention_bwd_ref(q, k, v, dout, *, causal, softmax_scale, cu_seqlens_q=None,
+                      cu_seqlens_k=None, kv_heads=None):
+    """Gradients of the forward of attention_ref: (dq, dk, dv) in float64.
+
+    Same layouts as attention_ref; dout has the layout of out.  A K/V head
+    shared by a group of query heads receives the sum of its group's
+    gradients (the chain rule over the consecutive-group map of "Deep Dive -
+    FlashAttention", "The public interface is several kernels").  kv_heads,
+    if given, restricts the work to those K/V heads and their query heads;
+    the other entries of dq, dk and dv are left at zero.
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    varlen = cu_seqlens_q is not None
+    if varlen != (cu_seqlens_k is not None):
+        raise ValueError("give both cu_seqlens arrays or neither")
+    if varlen:
+        q4, k4, v4, g4 = q[None], k[None], v[None], dout[None]
+    else:
+        q4, k4, v4, g4 = q, k, v, dout
+    hq_n, hkv_n = q4.shape[2], k4.shape[2]
+    kvmap = kv_head_for_queries(hq_n, hkv_n)
+    wanted = set(range(hkv_n)) if kv_heads is None else {int(h) for h in kv_heads}
+    dq = np.zeros_like(q4)
+    dk = np.zeros_like(k4)
+    dv = np.zeros_like(v4)
+    for b, qo, nq, ko, nk in _sequences(cu_seqlens_q, cu_seqlens_k, q4.shape[0], q4.shape[1], k4.shape[1]):
+        bb = 0 if varlen else b
+        for h in range(hq_n):
+            kvh = kvmap[h]
+            if kvh not in wanted:
+                continue
+            K = k4[bb, ko:ko + nk, kvh, :]
+            V = v4[bb, ko:ko + nk, kvh, :]
+            for r0 in range(0, nq, ROW_BLOCK):
+                r1 = min(nq, r0 + ROW_BLOCK)
+                keep = causal_keep(nq, nk)[r0:r1] if causal else None
+                gq, gk, gv = _attend_rows_bwd(q4[bb, qo + r0:qo + r1, h, :], K, V,
+                                              g4[bb, qo + r0:qo + r1, h, :], softmax_scale, keep)
+                dq[bb, qo + r0:qo + r1, h, :] = gq
+                dk[bb, ko:ko + nk, kvh, :] += gk
+                dv[bb, ko:ko + nk, kvh, :] += gv
+    if varlen:
+        return dq[0], dk[0], dv[0]
+    return dq, dk, dv
+
+
 __all__ = [
     "kv_head_for_queries", "causal_keep", "attention_ref", "attention_rows",
-    "paged_gather", "decode_ref", "ROW_BLOCK",
+    "paged_gather", "decode_ref", "attention_bwd_ref", "ROW_BLOCK",
 ]

@@ -375,9 +375,166 @@ def check_rows_api():
         assert np.max(np.abs(o[n] - out[b, i, h])) < 1e-12 and abs(l[n] - lse[b, h, i]) < 1e-12
 
 
+# ---- gradients ----------------------------------------------------------------
+
+def check_bwd_sdpa_fp64():
+    """Gradients against PyTorch autograd through its math backend in float64.
+
+    The check "Deep Dive - FlashAttention", "Backward recomputes tiles on
+    purpose" runs: shapes (2, 5), (5, 2) and (4, 4), 2 heads, d = 3, value
+    dim 4, an explicit bottom-right keep-mask (fully masked rows included) and
+    a random upstream gradient; agreement to 1e-12, and zero dq on rows with
+    no allowed key.
+    """
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    g = torch.Generator().manual_seed(7)
+    for nq, nk in [(2, 5), (5, 2), (4, 4)]:
+        q = torch.randn(1, 2, nq, 3, dtype=torch.float64, generator=g, requires_grad=True)
+        k = torch.randn(1, 2, nk, 3, dtype=torch.float64, generator=g, requires_grad=True)
+        v = torch.randn(1, 2, nk, 4, dtype=torch.float64, generator=g, requires_grad=True)
+        keep = torch.from_numpy(OA.causal_keep(nq, nk))
+        with sdpa_kernel(SDPBackend.MATH):
+            out = F.scaled_dot_product_attention(q, k, v, attn_mask=keep, dropout_p=0.0)
+        up = torch.randn(out.shape, dtype=torch.float64, generator=g)
+        tq, tk, tv = torch.autograd.grad(out, (q, k, v), up)
+        perm = lambda t: t.detach().permute(0, 2, 1, 3).numpy()  # noqa: E731
+        dq, dk, dv = OA.attention_bwd_ref(perm(q), perm(k), perm(v), perm(up), causal=True,
+                                          softmax_scale=1 / math.sqrt(3))
+        rows = keep.any(dim=1).numpy()
+        for mine, theirs in ((dq, tq), (dk, tk), (dv, tv)):
+            assert np.max(np.abs(mine - perm(theirs))) < 1e-12
+        assert np.all(dq[0, ~rows] == 0)
+
+
+def _loss_grad_fd(q, k, v, G, h, **kw):
+    """Central differences of L = sum(out * G) with respect to q, k and v."""
+    def loss(qq, kk, vv):
+        out, _ = OA.attention_ref(qq, kk, vv, **kw)
+        return float(np.sum(out * G))
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        base = args[which]
+        gr = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            old = base[idx]
+            base[idx] = old + h
+            lp = loss(*args)
+            base[idx] = old - h
+            lm = loss(*args)
+            base[idx] = old
+            gr[idx] = (lp - lm) / (2 * h)
+        grads.append(gr)
+    return grads
+
+
+def check_bwd_finite_differences():
+    """attention_bwd_ref equals the numerical derivative of attention_ref's output.
+
+    L = sum(out * G) for a random G, central differences with step 1e-5 on
+    tiny dense (MHA and GQA, causal with Nq < Nk, Nq > Nk and Nq = Nk, and
+    non-causal) and packed variable-length shapes; agreement to 1e-7.
+    """
+    rng = np.random.default_rng(21)
+    cases = [
+        dict(shape=(1, 3, 5, 2, 1, 2), causal=True),
+        dict(shape=(1, 4, 2, 2, 2, 3), causal=True),
+        dict(shape=(2, 3, 3, 2, 1, 2), causal=True),
+        dict(shape=(1, 3, 4, 1, 1, 3), causal=False),
+    ]
+    for c in cases:
+        B, nq, nk, hq, hkv, d = c["shape"]
+        q = rng.standard_normal((B, nq, hq, d))
+        k = rng.standard_normal((B, nk, hkv, d))
+        v = rng.standard_normal((B, nk, hkv, d + 1))
+        G = rng.standard_normal((B, nq, hq, d + 1))
+        kw = dict(causal=c["causal"], softmax_scale=0.7)
+        got = OA.attention_bwd_ref(q, k, v, G, **kw)
+        fd = _loss_grad_fd(q, k, v, G, 1e-5, **kw)
+        for a, b in zip(got, fd):
+            assert np.max(np.abs(a - b)) < 1e-7
+    # packed: two sequences (3 queries over 5 keys, 2 over 2)
+    cq, ck = np.array([0, 3, 5]), np.array([0, 5, 7])
+    q = rng.standard_normal((5, 2, 2))
+    k = rng.standard_normal((7, 1, 2))
+    v = rng.standard_normal((7, 1, 2))
+    G = rng.standard_normal((5, 2, 2))
+    kw = dict(causal=True, softmax_scale=0.9, cu_seqlens_q=cq, cu_seqlens_k=ck)
+    got = OA.attention_bwd_ref(q, k, v, G, **kw)
+    fd = _loss_grad_fd(q, k, v, G, 1e-5, **kw)
+    for a, b in zip(got, fd):
+        assert np.max(np.abs(a - b)) < 1e-7
+
+
+def check_bwd_identities():
+    """Closed forms that hold for any inputs.
+
+    The rows of dS sum to zero (softmax is shift invariant), so the key
+    gradients of every (sequence, K/V head) sum to the zero vector; the rows
+    of P sum to one, so the value gradients sum to the sum of the upstream
+    gradients over the rows that have a key; rows with no key get dq = 0.
+    """
+    rng = np.random.default_rng(5)
+    B, nq, nk, hq, hkv, d = 2, 7, 4, 6, 2, 5
+    q, k, v = (rng.standard_normal(s) for s in ((B, nq, hq, d), (B, nk, hkv, d), (B, nk, hkv, d)))
+    G = rng.standard_normal((B, nq, hq, d))
+    dq, dk, dv = OA.attention_bwd_ref(q, k, v, G, causal=True, softmax_scale=0.4)
+    keep = OA.causal_keep(nq, nk)
+    rows = keep.any(axis=1)
+    assert np.max(np.abs(dk.sum(axis=1))) < 1e-12
+    for b in range(B):
+        for kvh in range(hkv):
+            heads = range(kvh * (hq // hkv), (kvh + 1) * (hq // hkv))
+            want = sum(G[b, rows, h, :].sum(axis=0) for h in heads)
+            assert np.max(np.abs(dv[b, :, kvh, :].sum(axis=0) - want)) < 1e-12
+    assert np.all(dq[:, ~rows] == 0) and not rows.all()
+
+
+def check_bwd_gqa_and_packing():
+    """GQA equals MHA over consecutively repeated K/V with the copies' gradients
+    summed; a packed batch equals its sequences run one by one."""
+    rng = np.random.default_rng(8)
+    B, nq, nk, hq, hkv, d = 1, 5, 6, 6, 2, 3
+    q, k, v = (rng.standard_normal(s) for s in ((B, nq, hq, d), (B, nk, hkv, d), (B, nk, hkv, d)))
+    G = rng.standard_normal((B, nq, hq, d))
+    dq, dk, dv = OA.attention_bwd_ref(q, k, v, G, causal=True, softmax_scale=0.6)
+    rep = hq // hkv
+    kr, vr = np.repeat(k, rep, axis=2), np.repeat(v, rep, axis=2)
+    dq2, dk2, dv2 = OA.attention_bwd_ref(q, kr, vr, G, causal=True, softmax_scale=0.6)
+    assert np.max(np.abs(dq - dq2)) < 1e-12
+    assert np.max(np.abs(dk - dk2.reshape(B, nk, hkv, rep, d).sum(axis=3))) < 1e-12
+    assert np.max(np.abs(dv - dv2.reshape(B, nk, hkv, rep, d).sum(axis=3))) < 1e-12
+    lq, lk = [3, 0, 4], [5, 2, 3]
+    cq, ck = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((cq[-1], 4, 3))
+    k = rng.standard_normal((ck[-1], 2, 3))
+    v = rng.standard_normal((ck[-1], 2, 3))
+    G = rng.standard_normal((cq[-1], 4, 3))
+    dq, dk, dv = OA.attention_bwd_ref(q, k, v, G, causal=True, softmax_scale=0.5,
+                                      cu_seqlens_q=cq, cu_seqlens_k=ck)
+    for s in range(3):
+        a, bq = cq[s], cq[s + 1]
+        c, bk = ck[s], ck[s + 1]
+        e = OA.attention_bwd_ref(q[None, a:bq], k[None, c:bk], v[None, c:bk], G[None, a:bq],
+                                 causal=True, softmax_scale=0.5)
+        assert np.max(np.abs(dq[a:bq] - e[0][0]), initial=0) < 1e-12
+        assert np.max(np.abs(dk[c:bk] - e[1][0]), initial=0) < 1e-12
+        assert np.max(np.abs(dv[c:bk] - e[2][0]), initial=0) < 1e-12
+    # restricting to K/V heads leaves those heads' results unchanged
+    sub = OA.attention_bwd_ref(q, k, v, G, causal=True, softmax_scale=0.5,
+                               cu_seqlens_q=cq, cu_seqlens_k=ck, kv_heads=[1])
+    assert np.max(np.abs(sub[1][:, 1] - dk[:, 1])) < 1e-12 and np.all(sub[1][:, 0] == 0)
+    assert np.max(np.abs(sub[0][:, 2:] - dq[:, 2:])) < 1e-12 and np.all(sub[0][:, :2] == 0)
+
+
 ALL_CHECKS = [
     check_two_tiles_printed, check_tile_states, check_tiles_and_shifts, check_masked_rows,
     check_causal_masks_printed, check_gqa_printed, check_rows_sum_to_one, check_closed_forms,
     check_brute_force, check_sdpa_fp64, check_paged, check_split_combine,
     check_numpy_tiled_exactness, check_varlen_packing, check_rows_api,
+    check_bwd_sdpa_fp64, check_bwd_finite_differences, check_bwd_identities,
+    check_bwd_gqa_and_packing,
 ]

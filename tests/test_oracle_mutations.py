@@ -57,7 +57,67 @@ def _seqs_shared_k_offset(cu_q, cu_k, batch, nq, nk):
         yield b, qo, n_q, 0, n_k
 
 
+_orig_bwd_rows = OA._attend_rows_bwd
+_orig_bwd = OA.attention_bwd_ref
+
+
+def _bwd_parts(Q, K, V, G, scale, keep):
+    S = scale * (Q @ K.T)
+    if keep is not None:
+        S = np.where(keep, S, -np.inf)
+    mx = S.max(axis=1) if K.shape[0] else np.full(Q.shape[0], -np.inf)
+    ok = np.isfinite(mx)
+    E = np.exp(S - np.where(ok, mx, 0.0)[:, None])
+    P = E / np.where(ok, E.sum(axis=1), 1.0)[:, None]
+    P[~ok] = 0.0
+    return P, E, G @ V.T
+
+
+def _bwd_no_rowsum(Q, K, V, G, scale, keep):
+    P, _, dP = _bwd_parts(Q, K, V, G, scale, keep)
+    dS = P * dP
+    return scale * dS @ K, scale * dS.T @ Q, P.T @ G
+
+
+def _bwd_rowsum_of_dp(Q, K, V, G, scale, keep):
+    P, _, dP = _bwd_parts(Q, K, V, G, scale, keep)
+    dS = P * (dP - dP.sum(axis=1)[:, None])
+    return scale * dS @ K, scale * dS.T @ Q, P.T @ G
+
+
+def _bwd_dv_unnormalised(Q, K, V, G, scale, keep):
+    dq, dk, _ = _orig_bwd_rows(Q, K, V, G, scale, keep)
+    _, E, _ = _bwd_parts(Q, K, V, G, scale, keep)
+    return dq, dk, E.T @ G
+
+
+def _bwd_dq_transposed(Q, K, V, G, scale, keep):
+    P, _, dP = _bwd_parts(Q, K, V, G, scale, keep)
+    dS = P * (dP - (P * dP).sum(axis=1)[:, None])
+    _, dk, dv = _orig_bwd_rows(Q, K, V, G, scale, keep)
+    return scale * dS.T @ K, dk, dv
+
+
+def _bwd_group_not_summed(q, k, v, dout, **kw):
+    """K/V gradients from the last query head of each group only (overwrite, not sum)."""
+    dq, _, _ = _orig_bwd(q, k, v, dout, **kw)
+    hq, hkv = q.shape[-2], k.shape[-2]
+    g = np.array(dout, dtype=np.float64, copy=True)
+    for h in range(hq):
+        if (h + 1) % (hq // hkv):
+            g[..., h, :] = 0.0
+    _, dk, dv = _orig_bwd(q, k, v, g, **kw)
+    return dq, dk, dv
+
+
 MUTANTS = {
+    "bwd_no_rowsum_term": ("_attend_rows_bwd", _bwd_no_rowsum),
+    "bwd_rowsum_of_dp": ("_attend_rows_bwd", _bwd_rowsum_of_dp),
+    "bwd_dq_scale_dropped": ("_attend_rows_bwd", lambda Q, K, V, G, s, keep: (lambda a, b, c: (a / s, b, c))(*_orig_bwd_rows(Q, K, V, G, s, keep))),
+    "bwd_dk_scale_squared": ("_attend_rows_bwd", lambda Q, K, V, G, s, keep: (lambda a, b, c: (a, b * s, c))(*_orig_bwd_rows(Q, K, V, G, s, keep))),
+    "bwd_dv_unnormalised": ("_attend_rows_bwd", _bwd_dv_unnormalised),
+    "bwd_dq_transposed": ("_attend_rows_bwd", _bwd_dq_transposed),
+    "bwd_group_not_summed": ("attention_bwd_ref", _bwd_group_not_summed),
     "top_left_causal": ("causal_keep", lambda nq, nk: np.arange(nk)[None, :] <= np.arange(nq)[:, None]),
     "bottom_right_off_by_one": ("causal_keep", lambda nq, nk: np.arange(nk)[None, :] < np.arange(nq)[:, None] + nk - nq),
     "alternating_gqa": ("kv_head_for_queries", lambda hq, hkv: [h % hkv for h in range(hq)]),
