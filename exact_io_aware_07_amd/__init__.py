@@ -12,6 +12,7 @@ raises.
     part_o, part_l = attn_decode_splitkv(q, k_cache, v_cache, block_table, seqlens_k,
                                          chunk_tokens=c, num_splits=n, softmax_scale=s)
     out, lse = attn_decode_combine(part_o, part_l, seqlens_k, chunk_tokens=c)
+    dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, causal=True, softmax_scale=s)
 """
 import ctypes
 import os
@@ -19,7 +20,8 @@ import os
 import torch
 
 __all__ = [
-    "AttnError", "lib", "lib_path", "attn_fwd", "attn_decode_splitkv", "attn_decode_combine",
+    "AttnError", "lib", "lib_path", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+    "attn_decode_splitkv", "attn_decode_combine",
     "attn_decode", "attn_decode_num_splits", "attn_decode_default_chunk",
     "attn_decode_workspace_bytes", "attn_check_cu_seqlens", "attn_check_block_table",
     "STATUS",
@@ -42,6 +44,9 @@ _SIGNATURES = {
     "attn_status_str": ([_I], ctypes.c_char_p),
     "attn_last_error": ([], ctypes.c_char_p),
     "attn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                  _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
+    "attn_bwd_workspace_bytes": ([_I, _I], ctypes.c_size_t),
     "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "attn_decode_combine": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "attn_decode_num_splits": ([_I, _I], _I),
@@ -168,6 +173,75 @@ def attn_fwd(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=
                             _ptr(out), _ptr(lse), _stream(stream, dev))
     _check(st)
     return out, lse
+
+
+def attn_bwd_workspace_bytes(total_q, num_heads_q):
+    return lib().attn_bwd_workspace_bytes(int(total_q), int(num_heads_q))
+
+
+def attn_bwd(q, k, v, out, lse, dout, *, causal, softmax_scale, cu_seqlens_q=None,
+             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd from its saved out and lse and dout = dL/d(out).
+
+    Layouts as attn_fwd (out and dout like q, lse as attn_fwd returned it).
+    workspace: optional uint8 GPU tensor of at least attn_bwd_workspace_bytes(TQ, Hq)
+    bytes; allocated here when not given.
+    """
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need(t, name, torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if out.shape != q.shape or dout.shape != q.shape or v.shape != k.shape:
+        raise ValueError("out and dout must have q's shape, v k's shape")
+    varlen = cu_seqlens_q is not None
+    if varlen != (cu_seqlens_k is not None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    if varlen:
+        _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+        _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError("packed mode expects q [TQ,Hq,d] and k, v [TK,Hkv,d]")
+        if max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("packed mode needs max_seqlen_q and max_seqlen_k")
+        batch = cu_seqlens_q.numel() - 1
+        total_q, hq, d = q.shape
+        hkv = k.shape[1]
+        mq, mk = int(max_seqlen_q), int(max_seqlen_k)
+        lse_shape = (hq, total_q)
+    else:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("dense mode expects q [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d]")
+        batch, mq, hq, d = q.shape
+        mk, hkv = k.shape[1], k.shape[2]
+        total_q = batch * mq
+        lse_shape = (batch, hq, mq)
+    if tuple(lse.shape) != lse_shape:
+        raise ValueError(f"lse must have shape {lse_shape}")
+    outs = []
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty_like(like)
+        else:
+            _need(t, name, torch.bfloat16, dev)
+            if t.shape != like.shape:
+                raise ValueError(f"{name} has the wrong shape")
+        outs.append(t)
+    dq, dk, dv = outs
+    need = attn_bwd_workspace_bytes(total_q, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, dev)
+    if q.numel() == 0:
+        return dq, dk, dv
+    with torch.cuda.device(dev):
+        st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                            _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, mq, mk, total_q, hq, hkv,
+                            d, 1 if causal else 0, float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                            _ptr(workspace), workspace.numel(), _stream(stream, dev))
+    _check(st)
+    return dq, dk, dv
 
 
 def attn_decode_num_splits(max_seqlen_k, chunk_tokens):

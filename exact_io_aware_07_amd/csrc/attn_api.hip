@@ -126,6 +126,86 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, const int32_
                       "attn_fwd launch");
 }
 
+size_t attn_bwd_workspace_bytes(int total_q, int num_heads_q) {
+    if (total_q < 1 || num_heads_q < 1) return 0;
+    return (size_t)2 * total_q * num_heads_q * 4;
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int batch, int max_seqlen_q, int max_seqlen_k, int total_q, int num_heads_q,
+                       int num_heads_kv, int head_dim, int causal, float softmax_scale, void* dq,
+                       void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
+        return fail(ATTN_ERR_NULL, "every tensor argument of attn_bwd must be non-NULL");
+    const bool varlen = cu_seqlens_q != nullptr;
+    if (varlen != (cu_seqlens_k != nullptr))
+        return fail(ATTN_ERR_NULL, "cu_seqlens_q and cu_seqlens_k must both be NULL or both be set");
+    if (batch < 1 || max_seqlen_q < 1 || max_seqlen_k < (varlen ? 0 : 1) || num_heads_q < 1 ||
+        num_heads_kv < 1 || total_q < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d max_seqlen_q=%d max_seqlen_k=%d "
+                    "total_q=%d num_heads_q=%d num_heads_kv=%d", batch, max_seqlen_q, max_seqlen_k,
+                    total_q, num_heads_q, num_heads_kv);
+    if (!varlen && (long)total_q != (long)batch * max_seqlen_q)
+        return fail(ATTN_ERR_SHAPE, "dense mode needs total_q = batch * max_seqlen_q (%ld), got %d",
+                    (long)batch * max_seqlen_q, total_q);
+    if (num_heads_q % num_heads_kv)
+        return fail(ATTN_ERR_SHAPE, "num_heads_kv=%d does not divide num_heads_q=%d", num_heads_kv,
+                    num_heads_q);
+    if (head_dim != 64 && head_dim != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: head_dim=%d not in {64,128}", head_dim);
+    if (causal != 0 && causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1 (got %d)", causal);
+    attn_status_t st = check_scale(softmax_scale);
+    if (st != ATTN_OK) return st;
+    const size_t need = attn_bwd_workspace_bytes(total_q, num_heads_q);
+    if (workspace_bytes < need)
+        return fail(ATTN_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    // Outputs against inputs, the workspace and each other.  Byte ranges are
+    // known from total_q; packed K/V totals are not, so K-like ranges use
+    // start pointers only there.
+    const size_t qbytes = (size_t)total_q * num_heads_q * head_dim * 2;
+    const size_t lbytes = (size_t)total_q * num_heads_q * 4;
+    const size_t kbytes = varlen ? 1 : (size_t)batch * max_seqlen_k * num_heads_kv * head_dim * 2;
+    const void* ins_q[] = {q, out, dout};
+    for (const void* x : ins_q)
+        if (overlap(dq, qbytes, x, qbytes) || overlap(dk, kbytes, x, qbytes) || overlap(dv, kbytes, x, qbytes))
+            return fail(ATTN_ERR_ALIAS, "dq/dk/dv overlap an input");
+    const void* ins_k[] = {k, v};
+    for (const void* x : ins_k)
+        if (overlap(dq, qbytes, x, kbytes) || overlap(dk, kbytes, x, kbytes) || overlap(dv, kbytes, x, kbytes))
+            return fail(ATTN_ERR_ALIAS, "dq/dk/dv overlap an input");
+    if (overlap(dq, qbytes, lse, lbytes) || overlap(dk, kbytes, lse, lbytes) || overlap(dv, kbytes, lse, lbytes) ||
+        overlap(dq, qbytes, workspace, need) || overlap(dk, kbytes, workspace, need) ||
+        overlap(dv, kbytes, workspace, need) || overlap(dq, qbytes, dk, kbytes) ||
+        overlap(dq, qbytes, dv, kbytes) || overlap(dk, kbytes, dv, kbytes) ||
+        overlap(workspace, need, q, qbytes) || overlap(workspace, need, out, qbytes) ||
+        overlap(workspace, need, dout, qbytes) || overlap(workspace, need, lse, lbytes))
+        return fail(ATTN_ERR_ALIAS, "dq/dk/dv/workspace overlap an input or each other");
+    attn::BwdParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.out = static_cast<const uint16_t*>(out);
+    p.lse = lse;
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.dq = static_cast<uint16_t*>(dq);
+    p.dk = static_cast<uint16_t*>(dk);
+    p.dv = static_cast<uint16_t*>(dv);
+    p.lse2 = static_cast<float*>(workspace);
+    p.dsum = static_cast<float*>(workspace) + (size_t)total_q * num_heads_q;
+    p.batch = batch;
+    p.max_q = max_seqlen_q;
+    p.max_k = max_seqlen_k;
+    p.total_q = total_q;
+    p.hq = num_heads_q;
+    p.hkv = num_heads_kv;
+    p.scale = softmax_scale;
+    return hip_status(attn::launch_bwd(p, head_dim, causal != 0, varlen, static_cast<hipStream_t>(stream)),
+                      "attn_bwd launch");
+}
+
 attn_status_t attn_decode_splitkv(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_table, const int32_t* seqlens_k, int batch,
                                   int num_heads_q, int num_heads_kv, int head_dim, int page_size,

@@ -1,0 +1,548 @@
+// Backward pass of exact attention by recomputation (gfx950).
+//
+// "Deep Dive - FlashAttention", "Backward recomputes tiles on purpose": the
+// forward keeps Q, K, V, the output O and the row log-sum-exp; the backward
+// rebuilds each probability tile as P = exp(S - LSE) under the same mask and
+// forms, with G = dL/dO,
+//   dV = P^T G,   dP = G V^T,   dS = P * (dP - D),   D = rowsum(G * O),
+//   dQ = scale * dS K,   dK = scale * dS^T Q.
+// Masked probabilities, and their gradients, are zero.
+//
+// Three kernels:
+//   attn_bwd_prep_kernel  D per (row, query head), and lse in log2 units
+//                         (+inf for rows with no key, so their P is 0);
+//   attn_bwd_dkdv_kernel  one workgroup per (key tile, K/V head, sequence):
+//                         the tile's K and V stay in registers while the
+//                         query tiles of every query head of the group stream
+//                         through LDS; dK and dV accumulate in registers, so
+//                         no atomics and a fixed summation order;
+//   attn_bwd_dq_kernel    one workgroup per (query tile, query head,
+//                         sequence), shaped like the forward: K/V tiles stream
+//                         through LDS and dQ accumulates in registers.
+// All products are bf16 MFMA with fp32 accumulation; P and dS are rounded to
+// bf16 as the forward rounds P.
+
+#include "attn_tile.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+// Chunk swizzle for the backward's LDS tiles.  Each tile is read two ways:
+// as 32-row fragments (16 consecutive rows per 16-lane group, one 16-byte
+// chunk each) and with transposing 16-row reads (4 consecutive rows, four
+// chunks each).  Data chunk c of row r sits in slot c ^ swz_b(r); swz_b
+// takes all 16 values on 16 consecutive rows and moves each of 4 consecutive
+// rows to a different group of 4 slots, so both patterns are conflict-free.
+template <int CH>
+__device__ __forceinline__ uint32_t swz_b(uint32_t row) {
+    if constexpr (CH == 8) {
+        return (((row >> 1) & 1u) << 2) | ((row >> 2) & 3u);  // 128-byte rows: odd rows use the other banks
+    } else {
+        static_assert(CH == 16, "backward tiles support d = 64 and 128");
+        return ((row & 3u) << 2) | ((row >> 2) & 3u);
+    }
+}
+
+// Two row-major [ROWS, D] bf16 tiles (A then B) loaded HBM -> LDS with the
+// buffer range check zero-filling rows at or past nvalid.
+template <int D, int ROWS, int NW>
+struct BwdTile {
+    static constexpr uint32_t ROWB = 2 * D;
+    static constexpr int CH = D / 8;
+    static constexpr uint32_t A_BYTES = ROWS * ROWB;
+    static constexpr uint32_t BYTES = 2 * A_BYTES;
+    static constexpr int INSTR = A_BYTES / 1024;
+    static constexpr int PER_WAVE = INSTR / NW;
+    static constexpr int RPI = 1024 / ROWB;
+    static_assert(INSTR % NW == 0, "each wave issues the same number of loads");
+
+    __device__ __forceinline__ static void issue(const uint16_t* abase, const uint16_t* bbase,
+                                                 uint32_t stride_b, int nvalid, uint32_t st, int wave,
+                                                 int lane) {
+        const uint32_t nrec = nvalid > 0 ? (uint32_t)(nvalid < ROWS ? nvalid : ROWS) * stride_b : 0u;
+        const u32x4 ra = rsrc_words(abase, nrec);
+        const u32x4 rb = rsrc_words(bbase, nrec);
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int i = wave * PER_WAVE + j;
+            const uint32_t row = i * RPI + lane / CH;
+            const uint32_t off = row * stride_b + (((lane % CH) ^ swz_b<CH>(row)) * 16);
+            dma16(ra, st + i * 1024, off);
+            dma16(rb, st + A_BYTES + i * 1024, off);
+        }
+    }
+};
+
+// 32-row fragment (operand rows 32 rb + l % 32, d values 16 s + 8 (l / 32) ..
+// + 7) of a backward tile.
+template <int D>
+__device__ __forceinline__ u32x4 rd_row(const char* t, int rb, int s, int lane) {
+    const uint32_t row = 32 * rb + (lane & 31), c = 2 * s + (lane >> 5);
+    return lds_read16(t, row * (2 * D) + ((c ^ swz_b<D / 8>(row)) * 16));
+}
+
+// Transposed fragment: A operand whose rows are d (block db of 32) and whose
+// 16 contraction indices are tile rows of step c of the 32-row block rb, in
+// the order in which a 32x32 accumulator holds its rows (the order the
+// forward uses for V^T).
+template <int D>
+__device__ __forceinline__ u32x4 rd_tr(const char* t, int db, int rb, int c, int lane) {
+    constexpr int CH = D / 8;
+    const uint32_t G = lane >> 4, s = lane & 15;
+    const uint32_t d = 32 * db + 16 * (G & 1) + 4 * (s & 3);
+    const uint32_t r1 = 32 * rb + 16 * c + 4 * (G >> 1) + (s >> 2);
+    const uint32_t r2 = r1 + 8;
+    const uint32_t a1 = r1 * (2 * D) + (((d >> 3) ^ swz_b<CH>(r1)) * 16) + (d & 7) * 2;
+    const uint32_t a2 = r2 * (2 * D) + (((d >> 3) ^ swz_b<CH>(r2)) * 16) + (d & 7) * 2;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)(t + a1));
+    const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(__attribute__((address_space(3))) char*)(t + a2));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, x1), w2 = __builtin_bit_cast(u32x2, x2);
+    return u32x4{w1[0], w1[1], w2[0], w2[1]};
+}
+
+// Rows held by register r of a 32x32 accumulator in this lane.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// bf16 B operands (two 16-row steps) from a 32x32 accumulator.
+__device__ __forceinline__ void pack_acc(const f32x16& x, u32x4 (&w)[2]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[c][j] = pack_bf16x2(x[8 * c + 2 * j], x[8 * c + 2 * j + 1]);
+}
+
+// Write a [32 rows of d, 32 columns] accumulator block (scaled) as bf16 into
+// row `dst` of a [.., d] tensor: this lane's column, d values 32 db + 8 g +
+// 4 (l / 32) .. + 3.
+template <int DB>
+__device__ __forceinline__ void store_rows_bf16(uint16_t* dst, const f32x16 (&acc)[DB], float mul, int lane) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w = {pack_bf16x2(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                       pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+            *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * h) = w;
+        }
+}
+
+// ---- D = rowsum(G * O) and lse in log2 units ---------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
+    constexpr int LPI = D / 8;      // lanes per (row, head)
+    constexpr int IPW = 64 / LPI;   // items per wave
+    const int lane = threadIdx.x & 63;
+    const long item = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * IPW + lane / LPI;
+    const long n_items = (long)p.total_q * p.hq;
+    float x = 0.0f;
+    long row = 0;
+    int h = 0;
+    if (item < n_items) {
+        row = item / p.hq;
+        h = (int)(item % p.hq);
+        const long off = (row * p.hq + h) * D + (lane % LPI) * 8;
+        const u32x4 o = load16(p.out + off);
+        const u32x4 g = load16(p.dout + off);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x += __uint_as_float(o[j] << 16) * __uint_as_float(g[j] << 16);
+            x += __uint_as_float(o[j] & 0xffff0000u) * __uint_as_float(g[j] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int m = LPI / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    if (item < n_items && lane % LPI == 0) {
+        const long w = (long)h * p.total_q + row;
+        p.dsum[w] = x;
+        long li;
+        if (p.cu_q != nullptr) {
+            li = w;  // packed lse layout [hq, total_q]
+        } else {
+            const long b = row / p.max_q, i = row % p.max_q;
+            li = (b * p.hq + h) * p.max_q + i;
+        }
+        const float l = p.lse[li];
+        p.lse2[w] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    }
+}
+
+// ---- dK, dV ----------------------------------------------------------------
+// Wave w owns keys j0 + 32 w .. + 31 (lane l: key l % 32).  Per 64-row query
+// block: S = Q K^T and dP = G V^T (query rows x this wave's keys), P, dS, then
+// dV^T += G^T P and dK^T += Q^T dS with G and Q read transposed from LDS.
+template <int D, int NW, int WPE, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_bwd_dkdv_kernel(BwdParams p) {
+    constexpr int QBLK = 64;       // query rows per LDS stage
+    constexpr int KT = 32 * NW;    // keys per workgroup
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    using Tile = BwdTile<D, QBLK, NW>;
+    constexpr uint32_t STAGE = Tile::BYTES + 2 * QBLK * 4;  // Q, G, then lse2 and D of the block
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+
+    // Key tiles in ascending order: under a causal mask the first key tiles
+    // are seen by the most query rows, so the heaviest work starts first.
+    const int BH = p.batch * p.hkv;
+    const int kt = blockIdx.x / BH;
+    const int b = (blockIdx.x % BH) / p.hkv;
+    const int kvh = blockIdx.x % p.hkv;
+    int q_off, k_off, Nq, Nk;
+    if constexpr (VARLEN) {
+        q_off = p.cu_q[b];
+        Nq = p.cu_q[b + 1] - q_off;
+        k_off = p.cu_k[b];
+        Nk = p.cu_k[b + 1] - k_off;
+        Nq = Nq < 0 ? 0 : Nq;
+        Nk = Nk < 0 ? 0 : Nk;
+    } else {
+        q_off = b * p.max_q;
+        Nq = p.max_q;
+        k_off = b * p.max_k;
+        Nk = p.max_k;
+    }
+    const int j0 = kt * KT;
+    if (j0 >= Nk) return;
+    const int kw0 = j0 + 32 * wave;
+    const int key = kw0 + l32;
+    const int shift = Nk - Nq;  // causal: row i sees keys j <= i + shift
+
+    // K and V fragments (B operands), resident for the whole loop.
+    u32x4 kf[KS], vf[KS];
+    {
+        const long off = ((long)(k_off + key) * p.hkv + kvh) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 zk = {0u, 0u, 0u, 0u}, zv = {0u, 0u, 0u, 0u};
+            if (key < Nk) {
+                zk = load16(p.k + off + (2 * s + (lane >> 5)) * 8);
+                zv = load16(p.v + off + (2 * s + (lane >> 5)) * 8);
+            }
+            kf[s] = zk;
+            vf[s] = zv;
+        }
+    }
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dk[db][r] = 0.0f;
+            dv[db][r] = 0.0f;
+        }
+
+    // Query blocks that see at least one key of this workgroup.
+    const int g = p.hq / p.hkv;
+    int qb_lo = 0;
+    if constexpr (CAUSAL) {
+        const int i_min = j0 - shift;  // first row that sees key j0
+        qb_lo = i_min > 0 ? i_min / QBLK : 0;
+    }
+    const int qb_hi = (Nq + QBLK - 1) / QBLK;
+    const int n_qb = qb_hi > qb_lo ? qb_hi - qb_lo : 0;
+    const int n_it = g * n_qb;
+    const uint32_t stride_q = (uint32_t)p.hq * D * 2;
+    const float c2 = p.scale * kLog2e;
+
+    auto issue = [&](int it, char* st) __attribute__((always_inline)) {
+        const int h = kvh * g + it / n_qb;
+        const int qs = (qb_lo + it % n_qb) * QBLK;
+        const long off = ((long)(q_off + qs) * p.hq + h) * D;
+        Tile::issue(p.q + off, p.dout + off, stride_q, Nq - qs, lds_addr(st), wave, lane);
+        if (wave == 0) {
+            // lse2 rows to bytes [0, 256) after the tiles (lanes 0-15), D rows
+            // to [256, 512) (lanes 16-31): an LDS-DMA lane writes at the M0
+            // base + 16 * lane, and each instruction takes one range.
+            const int nv = Nq - qs < QBLK ? Nq - qs : QBLK;
+            const long w = (long)h * p.total_q + q_off + qs;
+            const uint32_t voff = (uint32_t)(lane & 15) * 16;
+            if (lane < 16) dma16(rsrc_words(p.lse2 + w, (uint32_t)nv * 4), lds_addr(st) + Tile::BYTES, voff);
+            if (lane >= 16 && lane < 32)
+                dma16(rsrc_words(p.dsum + w, (uint32_t)nv * 4), lds_addr(st) + Tile::BYTES, voff);
+        }
+    };
+
+    if (n_it > 0) issue(0, stage0);
+    wait_vmem();
+    __syncthreads();
+
+    auto step = [&](int it, char* cur, char* nxt) __attribute__((always_inline)) {
+        if (it + 1 < n_it) issue(it + 1, nxt);
+        const int qs = (qb_lo + it % n_qb) * QBLK;
+        // This wave's first key is seen from row kw0 - shift on.
+        const bool active = kw0 < Nk && (!CAUSAL || qs + QBLK - 1 >= kw0 - shift);
+        if (active) {
+            const char* qt = cur;
+            const char* gt = cur + Tile::A_BYTES;
+            const float* lv = reinterpret_cast<const float*>(cur + Tile::BYTES);
+            const bool need_mask = (qs + QBLK > Nq) || (kw0 + 31 >= Nk) ||
+                                   (CAUSAL && kw0 + 31 > qs + shift);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                f32x16 sacc, pacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[r] = 0.0f;
+                    pacc[r] = 0.0f;
+                }
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    sacc = mfma32(rd_row<D>(qt, rb, s, lane), kf[s], sacc);
+                    pacc = mfma32(rd_row<D>(gt, rb, s, lane), vf[s], pacc);
+                }
+                // lse2 and D of the 16 rows this lane holds: rows 32 rb + 8 q4 + 4 (l / 32) .. + 3.
+                f32x4 l2[4], dd[4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int r0 = 32 * rb + 8 * q4 + 4 * (lane >> 5);
+                    l2[q4] = *reinterpret_cast<const f32x4*>(lv + r0);
+                    dd[q4] = *reinterpret_cast<const f32x4*>(lv + QBLK + r0);
+                }
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = qs + 32 * rb + acc_row(r, lane);
+                        const bool keep = i < Nq && key < Nk && (!CAUSAL || key <= i + shift);
+                        if (!keep) sacc[r] = -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c2, -l2[r >> 2][r & 3]));
+                    sacc[r] = pr;
+                    pacc[r] = pr * (pacc[r] - dd[r >> 2][r & 3]);
+                }
+                u32x4 pp[2], pds[2];
+                pack_acc(sacc, pp);
+                pack_acc(pacc, pds);
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        dv[db] = mfma32(rd_tr<D>(gt, db, rb, c, lane), pp[c], dv[db]);
+                        dk[db] = mfma32(rd_tr<D>(qt, db, rb, c, lane), pds[c], dk[db]);
+                    }
+            }
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+    for (int it = 0; it < n_it; it += 2) {
+        step(it, stage0, stage1);
+        if (it + 1 < n_it) step(it + 1, stage1, stage0);
+    }
+
+    if (key < Nk) {
+        const long off = ((long)(k_off + key) * p.hkv + kvh) * D;
+        store_rows_bf16<DB>(p.dk + off, dk, p.scale, lane);
+        store_rows_bf16<DB>(p.dv + off, dv, 1.0f, lane);
+    }
+}
+
+// ---- dQ ------------------------------------------------------------------------
+// Shaped like the forward: wave w owns query rows q0 + 32 w .. + 31 (lane l:
+// row l % 32).  Per 64-key tile: S^T = K Q^T and dP^T = V G^T, P^T, dS^T,
+// then dQ^T += K^T dS^T with K read transposed from LDS.
+template <int D, int NW, int WPE, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void attn_bwd_dq_kernel(BwdParams p) {
+    constexpr int BC = 64;
+    constexpr int KB = BC / 32;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int BR = 32 * NW;
+    using Tile = BwdTile<D, BC, NW>;
+    __shared__ __attribute__((aligned(1024))) char stage0[Tile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage1[Tile::BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+
+    // Heaviest query tiles first.
+    const int BH = p.batch * p.hq;
+    const int qt = p.n_tiles - 1 - (int)(blockIdx.x / BH);
+    const int b = (blockIdx.x % BH) / p.hq;
+    const int hq = blockIdx.x % p.hq;
+    const int kvh = hq / (p.hq / p.hkv);
+    int q_off, k_off, Nq, Nk;
+    if constexpr (VARLEN) {
+        q_off = p.cu_q[b];
+        Nq = p.cu_q[b + 1] - q_off;
+        k_off = p.cu_k[b];
+        Nk = p.cu_k[b + 1] - k_off;
+        Nq = Nq < 0 ? 0 : Nq;
+        Nk = Nk < 0 ? 0 : Nk;
+    } else {
+        q_off = b * p.max_q;
+        Nq = p.max_q;
+        k_off = b * p.max_k;
+        Nk = p.max_k;
+    }
+    const int q0 = qt * BR;
+    if (q0 >= Nq) return;
+    int n_tiles = (Nk + BC - 1) / BC;
+    if constexpr (CAUSAL) {
+        const int kmax = min(q0 + BR, Nq) - 1 + Nk - Nq;
+        n_tiles = kmax < 0 ? 0 : min(n_tiles, kmax / BC + 1);
+    }
+    const uint32_t stride_k = (uint32_t)p.hkv * D * 2;
+    const uint16_t* kbase = p.k + ((long)k_off * p.hkv + kvh) * D;
+    const uint16_t* vbase = p.v + ((long)k_off * p.hkv + kvh) * D;
+
+    const int wr0 = q0 + 32 * wave;
+    const bool wave_rows = wr0 < Nq;
+    const int w_last_key = min(wr0 + 32, Nq) - 1 + Nk - Nq;
+    const int w_first_key_lim = wr0 + Nk - Nq;
+    const int row = wr0 + l32;
+
+    // Q^T and G^T fragments (B operands), and this row's lse2 and D.
+    u32x4 qf[KS], gf[KS];
+    float l2 = INFINITY, dd = 0.0f;
+    {
+        const long off = ((long)(q_off + row) * p.hq + hq) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 zq = {0u, 0u, 0u, 0u}, zg = {0u, 0u, 0u, 0u};
+            if (row < Nq) {
+                zq = load16(p.q + off + (2 * s + (lane >> 5)) * 8);
+                zg = load16(p.dout + off + (2 * s + (lane >> 5)) * 8);
+            }
+            qf[s] = zq;
+            gf[s] = zg;
+        }
+        if (row < Nq) {
+            const long w = (long)hq * p.total_q + q_off + row;
+            l2 = p.lse2[w];
+            dd = p.dsum[w];
+        }
+    }
+    f32x16 dacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dacc[db][r] = 0.0f;
+    const float c2 = p.scale * kLog2e;
+
+    if (n_tiles > 0) Tile::issue(kbase, vbase, stride_k, Nk, lds_addr(stage0), wave, lane);
+    wait_vmem();
+    __syncthreads();
+
+    auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
+        const char* ks = cur;
+        const char* vs = cur + Tile::A_BYTES;
+        if (t + 1 < n_tiles) {
+            const long off = (long)(t + 1) * BC * p.hkv * D;
+            Tile::issue(kbase + off, vbase + off, stride_k, Nk - (t + 1) * BC, lds_addr(nxt), wave, lane);
+        }
+        const int k0 = t * BC;
+        const bool active = wave_rows && (!CAUSAL || k0 <= w_last_key);
+        if (active) {
+            const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > w_first_key_lim);
+            const int lim = CAUSAL ? min(Nk - 1, row + Nk - Nq) : Nk - 1;
+            // One 32-key block at a time keeps two accumulators live, not four.
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x16 sacc, pacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    sacc[r] = 0.0f;
+                    pacc[r] = 0.0f;
+                }
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    sacc = mfma32(rd_row<D>(ks, kb, s, lane), qf[s], sacc);
+                    pacc = mfma32(rd_row<D>(vs, kb, s, lane), gf[s], pacc);
+                }
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (k0 + 32 * kb + acc_row(r, lane) > lim) sacc[r] = -INFINITY;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c2, -l2));
+                    pacc[r] = pr * (pacc[r] - dd);
+                }
+                u32x4 pds[2];
+                pack_acc(pacc, pds);
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        dacc[db] = mfma32(rd_tr<D>(ks, db, kb, c, lane), pds[c], dacc[db]);
+            }
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, stage0, stage1);
+        if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
+    }
+
+    if (row < Nq) store_rows_bf16<DB>(p.dq + ((long)(q_off + row) * p.hq + hq) * D, dacc, p.scale, lane);
+}
+
+// ---- launchers -------------------------------------------------------------------
+template <int D, bool CAUSAL, bool VARLEN>
+static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
+    constexpr int DKDV_NW = 4, DKDV_WPE = D <= 64 ? 2 : 1;
+    constexpr int DQ_NW = 8, DQ_WPE = 2;
+    BwdParams p = p0;
+    {
+        constexpr int IPB = 4 * (64 / (D / 8));  // (row, head) items per block
+        const long items = (long)p.total_q * p.hq;
+        const long grid = (items + IPB - 1) / IPB;
+        if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        if (grid > 0) hipLaunchKernelGGL(attn_bwd_prep_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        constexpr int KT = 32 * DKDV_NW;
+        p.n_tiles = (p.max_k + KT - 1) / KT;
+        const long grid = (long)p.n_tiles * p.batch * p.hkv;
+        if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        if (grid > 0)
+            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DKDV_NW, DKDV_WPE, CAUSAL, VARLEN>), dim3((unsigned)grid),
+                               dim3(DKDV_NW * 64), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        constexpr int BR = 32 * DQ_NW;
+        p.n_tiles = (p.max_q + BR - 1) / BR;
+        const long grid = (long)p.n_tiles * p.batch * p.hq;
+        if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        if (grid > 0)
+            hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DQ_NW, DQ_WPE, CAUSAL, VARLEN>), dim3((unsigned)grid),
+                               dim3(DQ_NW * 64), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdParams& p, bool causal, bool varlen, hipStream_t s) {
+    if (causal) return varlen ? launch_bwd_cfg<D, true, true>(p, s) : launch_bwd_cfg<D, true, false>(p, s);
+    return varlen ? launch_bwd_cfg<D, false, true>(p, s) : launch_bwd_cfg<D, false, false>(p, s);
+}
+
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_bwd_d<64>(p, causal, varlen, s);
+        case 128: return launch_bwd_d<128>(p, causal, varlen, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn

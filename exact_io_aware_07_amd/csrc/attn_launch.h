@@ -40,7 +40,27 @@ struct CombineParams {
     int batch, hq, chunk, n_splits;
 };
 
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;
+    const float* lse;
+    const uint16_t* dout;
+    const int32_t* cu_q;  // null in dense mode
+    const int32_t* cu_k;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    float* lse2;  // workspace [hq][total_q]: lse * log2(e), +inf for rows with no key
+    float* dsum;  // workspace [hq][total_q]: rowsum(dout * out)
+    int batch, max_q, max_k, total_q, hq, hkv;
+    int n_tiles;  // filled in by the launchers (query tiles or key tiles)
+    float scale;
+};
+
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_decode_combine(const CombineParams& p, int head_dim, hipStream_t s);
 

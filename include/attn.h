@@ -102,6 +102,45 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v,
                        void* out, float* lse, void* stream);
 
 /*
+ * attn_bwd -- gradients of attn_fwd by recomputation.
+ *
+ * From the forward's saved q, k, v, out and lse and the upstream gradient
+ * dout = dL/d(out), rebuild each probability tile as exp(S - lse) under the
+ * same mask and form dV = P^T dout, dP = dout V^T, dS = P * (dP - D) with
+ * D = rowsum(dout * out), dQ = scale * dS K, dK = scale * dS^T Q ("Deep Dive
+ * - FlashAttention", "Backward recomputes tiles on purpose").  A K/V head
+ * shared by a group of query heads receives the sum over its group.  Rows
+ * with no allowed key (lse = -inf) contribute nothing.
+ *
+ * Layouts and modes are those of attn_fwd: q, out, dout, dq like q; k, v, dk,
+ * dv like k; lse as attn_fwd wrote it (required, not NULL).  total_q is the
+ * number of query rows: batch * max_seqlen_q in dense mode, the packed total
+ * TQ = cu_seqlens_q[batch] in packed mode (the caller knows it from the size
+ * of q; a different value is undefined behaviour).
+ * workspace: device memory of at least attn_bwd_workspace_bytes(total_q,
+ *   num_heads_q) bytes, owned by the caller; its contents on entry do not
+ *   matter and it is overwritten.
+ * dq, dk, dv (bf16, written; round to nearest even) must not overlap any
+ * input, the workspace or each other.  Calls that share a workspace on one
+ * stream are ordered; on different streams they race.
+ * Requirements: those of attn_fwd, and head_dim in {64, 128}
+ * (ATTN_ERR_UNSUPPORTED otherwise); workspace_bytes too small gives
+ * ATTN_ERR_SHAPE.  Errors are returned before anything is enqueued.
+ */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                       const float* lse, const void* dout,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                       int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                       int num_heads_q, int num_heads_kv, int head_dim,
+                       int causal, float softmax_scale,
+                       void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_bwd needs: two float32 values (the row sum D and the
+ * base-2 lse) per query row and query head; 0 for non-positive sizes. */
+size_t attn_bwd_workspace_bytes(int total_q, int num_heads_q);
+
+/*
  * attn_decode_splitkv -- one-token decode over a paged KV cache, split along
  * the cached keys ("FlashAttention-3 and PagedAttention: IO-Aware Attention
  * Kernels (2026)", "Why decode starves the GPU" and "How GQA and MLA reshape

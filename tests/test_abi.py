@@ -102,6 +102,41 @@ def test_decode_combine_rejects(kw, code):
     assert comb(**kw) == code
 
 
+DQ = ctypes.c_void_p(0x60000000)
+DK = ctypes.c_void_p(0x70000000)
+DV = ctypes.c_void_p(0x78000000)
+WS = ctypes.c_void_p(0x7c000000)
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, out=OUT, lse=LSE, dout=ctypes.c_void_p(0x58000000), cq=NULL,
+             ck=NULL, batch=1, mq=8, mk=8, tq=8, hq=4, hkv=2, d=128, causal=1, scale=0.125, dq=DQ,
+             dk=DK, dv=DV, ws=WS, wsb=8 * 8 * 4)
+    a.update(kw)
+    return ea.lib().attn_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["cq"], a["ck"],
+                             a["batch"], a["mq"], a["mk"], a["tq"], a["hq"], a["hkv"], a["d"],
+                             a["causal"], a["scale"], a["dq"], a["dk"], a["dv"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(lse=NULL), 1), (dict(dout=NULL), 1), (dict(dv=NULL), 1), (dict(ws=NULL), 1),
+    (dict(ck=FAKE), 1),
+    (dict(batch=0), 2), (dict(tq=0), 2), (dict(tq=9), 2), (dict(hq=6, hkv=4), 2), (dict(causal=3), 2),
+    (dict(wsb=8 * 8 * 4 - 1), 2),
+    (dict(d=256), 3), (dict(d=96), 3),
+    (dict(scale=0.0), 4),
+    (dict(dq=FAKE), 5), (dict(dk=FAKE3), 5), (dict(dv=DK), 5), (dict(ws=DQ), 5), (dict(dq=OUT), 5),
+])
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_bytes():
+    lib = ea.lib()
+    assert lib.attn_bwd_workspace_bytes(1000, 32) == 2 * 1000 * 32 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 32) == 0 and lib.attn_bwd_workspace_bytes(5, -1) == 0
+
+
 def test_host_helpers():
     assert ea.attn_decode_num_splits(32768, 2048) == 16
     assert ea.attn_decode_num_splits(32769, 2048) == 17
