@@ -158,6 +158,34 @@ def write_traffic(fetch_csv, write_csv, copy_mib, commands):
     return 0
 
 
+def time_backward(ea, pc, out, lse, stream, torch, reps=10):
+    """attn_bwd on the prefill workload, timed apart from the step.
+
+    Gradients are a widening of the path (not part of the step above).  FLOPs
+    follow the usual convention of 2.5x the forward's (five products of the
+    forward's size: two recomputed, three gradient products).
+    """
+    g = torch.Generator(device=pc["q"].device).manual_seed(99)
+    dout = torch.randn(pc["q"].shape, generator=g, device=pc["q"].device).to(torch.bfloat16)
+    total_q = pc["B"] * pc["Nq"]
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(total_q, pc["Hq"]), dtype=torch.uint8, device=pc["q"].device)
+    dq, dk, dv = (torch.empty_like(pc[x]) for x in "qkv")
+    kw = dict(causal=pc["causal"], softmax_scale=pc["scale"], dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+    for _ in range(3):
+        ea.attn_bwd(pc["q"], pc["k"], pc["v"], out, lse, dout, **kw)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        ea.attn_bwd(pc["q"], pc["k"], pc["v"], out, lse, dout, **kw)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    flops = 2.5 * prefill_flops(pc)
+    return {"kernel_ms_mean": round(ms, 4), "value": round(flops / (ms * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s", "flops": flops, "flops_convention": "2.5x the forward metric FLOPs",
+            "workload": PREFILL}
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
     import numpy as np
@@ -213,6 +241,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the separately timed attn_bwd leg (not part of the step)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for counter scaling)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -300,6 +330,7 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    bwd = None if args.no_backward else time_backward(ea, pc, out, lse, stream, torch)
     pre = [e[0].elapsed_time(e[1]) for e in events]
     spl = [e[1].elapsed_time(e[2]) for e in events]
     cmb = [e[2].elapsed_time(e[3]) for e in events]
@@ -354,6 +385,8 @@ def main():
                    "hip": getattr(torch.version, "hip", None)},
         "kernel_source_digest": digest,
     }
+    if bwd is not None:
+        rec["backward"] = bwd
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pc)
     print(json.dumps(rec), flush=True)
