@@ -8,7 +8,8 @@ with NumPy, one (sequence, query head) at a time.
 Sources (page title, section):
   * "Deep Dive - FlashAttention": "Exact attention without an n x n workspace",
     "Two tiles by hand", "The public interface is several kernels",
-    "Backward recomputes tiles on purpose" (the gradients),
+    "Backward recomputes tiles on purpose" (the gradients), "Causal 2.1 is the
+    decode gotcha" (the local window),
     "Causal 2.1 is the decode gotcha", "Paged KV is a lookup, not a cache manager".
   * "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)":
     "Runnable Example: Measuring the IO Gap", "Decode-Time Kernels".
@@ -28,4 +29,6 @@ from .attention import (  # noqa: F401
     paged_gather,
     decode_ref,
     attention_bwd_ref,
+    window_keep,
+    paged_prefill_ref,
 )

@@ -42,6 +42,38 @@ def causal_keep(seqlen_q, seqlen_k):
     return j <= i + (seqlen_k - seqlen_q)
 
 
+def window_keep(seqlen_q, seqlen_k, left, right):
+    """Local-window keep-mask, shape [seqlen_q, seqlen_k].
+
+    "Deep Dive - FlashAttention", "Causal 2.1 is the decode gotcha": a finite
+    window (left, right) lets query row i see key j when
+    i + seqlen_k - seqlen_q - left <= j <= i + seqlen_k - seqlen_q + right
+    (clipped to the real keys); a side given as -1 is unbounded.
+    """
+    i = np.arange(seqlen_q)[:, None]
+    j = np.arange(seqlen_k)[None, :]
+    c = i + (seqlen_k - seqlen_q)
+    keep = np.ones((seqlen_q, seqlen_k), dtype=bool)
+    if left >= 0:
+        keep &= j >= c - left
+    if right >= 0:
+        keep &= j <= c + right
+    return keep
+
+
+def _keep(seqlen_q, seqlen_k, causal, window):
+    """Combined keep-mask (None when everything is kept): causal masking
+    further restricts a window's set (same section)."""
+    left, right = window
+    keep = None
+    if causal:
+        keep = causal_keep(seqlen_q, seqlen_k)
+    if left >= 0 or right >= 0:
+        w = window_keep(seqlen_q, seqlen_k, left, right)
+        keep = w if keep is None else keep & w
+    return keep
+
+
 def _attend_rows(Q, K, V, scale, keep):
     """Attention for a block of query rows against one key/value head.
 
@@ -93,7 +125,8 @@ def _sequences(cu_seqlens_q, cu_seqlens_k, batch, nq, nk):
             yield b, cq[b], cq[b + 1] - cq[b], ck[b], ck[b + 1] - ck[b]
 
 
-def attention_ref(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None):
+def attention_ref(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None,
+                  window=(-1, -1)):
     """Full forward: (out, lse) in float64.
 
     Dense layout ("Deep Dive - FlashAttention", "The public interface is
@@ -104,7 +137,8 @@ def attention_ref(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqle
     cache manager"): q [total_q, Hq, d], k and v [total_k, Hkv, d] with int32
     cumulative offsets cu_seqlens_q / cu_seqlens_k of batch + 1 entries;
     returns out [total_q, Hq, d] and lse [Hq, total_q].  Causal masking is
-    bottom-right aligned per sequence, with that sequence's own lengths.
+    bottom-right aligned per sequence, with that sequence's own lengths, and
+    so is the optional local window (left, right) (window_keep).
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     varlen = cu_seqlens_q is not None
@@ -123,9 +157,10 @@ def attention_ref(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqle
         for h in range(hq_n):
             K = k4[bb, ko:ko + nk, kvmap[h], :]
             V = v4[bb, ko:ko + nk, kvmap[h], :]
+            full = _keep(nq, nk, causal, window)
             for r0 in range(0, nq, ROW_BLOCK):
                 r1 = min(nq, r0 + ROW_BLOCK)
-                keep = causal_keep(nq, nk)[r0:r1] if causal else None
+                keep = None if full is None else full[r0:r1]
                 o, s = _attend_rows(q4[bb, qo + r0:qo + r1, h, :], K, V, softmax_scale, keep)
                 out[bb, qo + r0:qo + r1, h, :] = o
                 lse[bb, h, qo + r0:qo + r1] = s
@@ -134,7 +169,8 @@ def attention_ref(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqle
     return out, lse
 
 
-def attention_rows(q, k, v, rows, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None):
+def attention_rows(q, k, v, rows, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None,
+                   window=(-1, -1)):
     """The same definition evaluated for selected outputs only.
 
     rows: iterable of (seq, q_head, i) with i the row index inside the
@@ -158,7 +194,8 @@ def attention_rows(q, k, v, rows, *, causal, softmax_scale, cu_seqlens_q=None, c
             Q = _as64(q[b, i, h, :])[None]
             K = _as64(k[b, :, kvmap[h], :])
             V = _as64(v[b, :, kvmap[h], :])
-        keep = causal_keep(nq, nk)[i:i + 1] if causal else None
+        full = _keep(nq, nk, causal, window)
+        keep = None if full is None else full[i:i + 1]
         o, s = _attend_rows(Q, K, V, softmax_scale, keep)
         outs.append(o[0])
         lses.append(s[0])
@@ -246,6 +283,41 @@ def _attend_rows_bwd(Q, K, V, G, scale, keep):
     return dQ, dK, dV
 
 
+def paged_prefill_ref(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, *, causal,
+                      softmax_scale, window=(-1, -1), sequences=None):
+    """Prefill of new query rows against a paged cache that already holds them.
+
+    q [total_q, Hq, d] packed with cu_seqlens_q; k_cache, v_cache
+    [num_pages, page_size, Hkv, d]; block_table [B, max_pages]; seqlens_k [B]
+    cached keys per sequence, the last of which belong to that sequence's new
+    rows (so masks align bottom-right).  Each sequence's keys are gathered
+    through its table row ("Deep Dive - FlashAttention", "Paged KV is a
+    lookup, not a cache manager"; "FlashAttention-3 and PagedAttention:
+    IO-Aware Attention Kernels (2026)", "Block tables and what the kernel
+    does") and attended as in attention_ref.  Returns out [total_q, Hq, d] and
+    lse [Hq, total_q]; `sequences` restricts the work (other rows stay 0 /
+    -inf).
+    """
+    hq_n, hkv_n = q.shape[1], k_cache.shape[2]
+    kvmap = kv_head_for_queries(hq_n, hkv_n)
+    cq = [int(x) for x in np.asarray(cu_seqlens_q)]
+    out = np.zeros((q.shape[0], hq_n, v_cache.shape[3]))
+    lse = np.full((hq_n, q.shape[0]), -np.inf)
+    seqs = range(len(cq) - 1) if sequences is None else sequences
+    for b in seqs:
+        nq, nk = cq[b + 1] - cq[b], int(seqlens_k[b])
+        table = [int(x) for x in np.asarray(block_table[b])]
+        full = _keep(nq, nk, causal, window)
+        for kvh in range(hkv_n):
+            K = _as64(paged_gather(k_cache[:, :, kvh, :], table, nk))
+            V = _as64(paged_gather(v_cache[:, :, kvh, :], table, nk))
+            for h in [h for h in range(hq_n) if kvmap[h] == kvh]:
+                o, s = _attend_rows(_as64(q[cq[b]:cq[b + 1], h, :]), K, V, softmax_scale, full)
+                out[cq[b]:cq[b + 1], h] = o
+                lse[h, cq[b]:cq[b + 1]] = s
+    return out, lse
+
+
 def attention_bwd_ref(q, k, v, dout, *, causal, softmax_scale, cu_seqlens_q=None,
                       cu_seqlens_k=None, kv_heads=None):
     """Gradients of the forward of attention_ref: (dq, dk, dv) in float64.
@@ -294,5 +366,6 @@ def attention_bwd_ref(q, k, v, dout, *, causal, softmax_scale, cu_seqlens_q=None
 
 __all__ = [
     "kv_head_for_queries", "causal_keep", "attention_ref", "attention_rows",
-    "paged_gather", "decode_ref", "attention_bwd_ref", "ROW_BLOCK",
+    "paged_gather", "decode_ref", "attention_bwd_ref", "window_keep", "paged_prefill_ref",
+    "ROW_BLOCK",
 ]

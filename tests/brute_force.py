@@ -38,8 +38,13 @@ def _row(qrow, keys, vals, allowed, scale, dv):
     return out, lse
 
 
-def brute_attention(q, k, v, *, causal, scale, cu_q=None, cu_k=None):
-    """q, k, v as nested Python lists in the dense [B,N,H,d] or packed [T,H,d] layout."""
+def brute_attention(q, k, v, *, causal, scale, cu_q=None, cu_k=None, window=(-1, -1)):
+    """q, k, v as nested Python lists in the dense [B,N,H,d] or packed [T,H,d] layout.
+
+    window (left, right): key j is allowed for row i when i + nk - nq - left
+    <= j <= i + nk - nq + right, a side of -1 being unbounded ("Deep Dive -
+    FlashAttention", "Causal 2.1 is the decode gotcha").
+    """
     if cu_q is None:
         seqs = [(b, 0, len(q[b]), 0, len(k[b])) for b in range(len(q))]
         getq = lambda b, i, h: q[b][i][h]
@@ -66,7 +71,11 @@ def brute_attention(q, k, v, *, causal, scale, cu_q=None, cu_k=None):
             keys = [getk(b, ko + j, kvh) for j in range(nk)]
             vals = [getv(b, ko + j, kvh) for j in range(nk)]
             for i in range(nq):
-                allowed = [j for j in range(nk) if (not causal) or j - i <= nk - nq]
+                c = i + nk - nq
+                allowed = [j for j in range(nk)
+                           if ((not causal) or j <= c)
+                           and (window[0] < 0 or j >= c - window[0])
+                           and (window[1] < 0 or j <= c + window[1])]
                 o, s = _row(getq(b, qo + i, h), keys, vals, allowed, scale, dv)
                 out[(b, i, h)] = o
                 lse[(b, i, h)] = s

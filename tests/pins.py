@@ -375,6 +375,121 @@ def check_rows_api():
         assert np.max(np.abs(o[n] - out[b, i, h])) < 1e-12 and abs(l[n] - lse[b, h, i]) < 1e-12
 
 
+# ---- local window and paged prefill ------------------------------------------------
+
+def check_window_forms():
+    """Special cases of the window rule of "Deep Dive - FlashAttention",
+    "Causal 2.1 is the decode gotcha": (-1, -1) is no window; (-1, 0) is the
+    bottom-right causal mask; with causal on, a right side >= 0 changes
+    nothing; (0, 0) keeps exactly key i + Nk - Nq, so the row returns that
+    value row and lse equals that score (or is empty when the key is out of
+    range)."""
+    rng = np.random.default_rng(17)
+    for nq, nk in [(5, 9), (9, 5), (6, 6)]:
+        q = rng.standard_normal((1, nq, 2, 3))
+        k = rng.standard_normal((1, nk, 1, 3))
+        v = rng.standard_normal((1, nk, 1, 4))
+        for causal in (False, True):
+            a = OA.attention_ref(q, k, v, causal=causal, softmax_scale=0.8)
+            b = OA.attention_ref(q, k, v, causal=causal, softmax_scale=0.8, window=(-1, -1))
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        a = OA.attention_ref(q, k, v, causal=True, softmax_scale=0.8)
+        b = OA.attention_ref(q, k, v, causal=False, softmax_scale=0.8, window=(-1, 0))
+        c = OA.attention_ref(q, k, v, causal=True, softmax_scale=0.8, window=(-1, 3))
+        for x in (b, c):
+            assert np.array_equal(a[0], x[0]) and np.array_equal(a[1], x[1])
+        o, l = OA.attention_ref(q, k, v, causal=False, softmax_scale=0.8, window=(0, 0))
+        for i in range(nq):
+            j = i + nk - nq
+            for h in range(2):
+                if 0 <= j < nk:
+                    assert np.max(np.abs(o[0, i, h] - v[0, j, 0])) < 1e-12
+                    assert abs(l[0, h, i] - 0.8 * q[0, i, h] @ k[0, j, 0]) < 1e-12
+                else:
+                    assert np.all(o[0, i, h] == 0) and np.isneginf(l[0, h, i])
+
+
+def check_window_brute_force(seed=3, n_cases=24):
+    """Windowed attention against the scalar loops (dense and packed)."""
+    rng = np.random.default_rng(seed)
+    for case in range(n_cases):
+        hkv = int(rng.choice([1, 2]))
+        hq = hkv * int(rng.choice([1, 2]))
+        d = int(rng.integers(1, 6))
+        causal = bool(case % 2)
+        window = (int(rng.integers(-1, 5)), int(rng.integers(-1, 5)))
+        scale = float(rng.uniform(0.2, 1.2))
+        if case % 3 == 2:
+            nqs = [int(x) for x in rng.integers(0, 7, size=3)]
+            nks = [int(x) for x in rng.integers(0, 7, size=3)]
+            cq = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32)
+            ck = np.concatenate([[0], np.cumsum(nks)]).astype(np.int32)
+            q = rng.standard_normal((int(cq[-1]), hq, d))
+            k = rng.standard_normal((int(ck[-1]), hkv, d))
+            v = rng.standard_normal((int(ck[-1]), hkv, d))
+            out, lse = OA.attention_ref(q, k, v, causal=causal, softmax_scale=scale,
+                                        cu_seqlens_q=cq, cu_seqlens_k=ck, window=window)
+            bo, bl = brute_attention(_tolist(q), _tolist(k), _tolist(v), causal=causal, scale=scale,
+                                     cu_q=cq.tolist(), cu_k=ck.tolist(), window=window)
+            for (sq, i, h), o in bo.items():
+                row = int(cq[sq]) + i
+                assert np.max(np.abs(out[row, h] - np.array(o)), initial=0.0) < 1e-12
+                ref = bl[(sq, i, h)]
+                assert (lse[h, row] == ref) if math.isinf(ref) else abs(lse[h, row] - ref) < 1e-12
+        else:
+            nq, nk = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+            q = rng.standard_normal((1, nq, hq, d))
+            k = rng.standard_normal((1, nk, hkv, d))
+            v = rng.standard_normal((1, nk, hkv, d))
+            out, lse = OA.attention_ref(q, k, v, causal=causal, softmax_scale=scale, window=window)
+            bo, bl = brute_attention(_tolist(q), _tolist(k), _tolist(v), causal=causal, scale=scale,
+                                     window=window)
+            for (b, i, h), o in bo.items():
+                assert np.max(np.abs(out[b, i, h] - np.array(o))) < 1e-12, (case, window)
+                ref = bl[(b, i, h)]
+                assert (lse[b, h, i] == ref) if math.isinf(ref) else abs(lse[b, h, i] - ref) < 1e-12
+
+
+def check_paged_prefill():
+    """Prefill through a shuffled block table equals packed attention over the
+    same keys laid out contiguously; with one new row per sequence and no
+    window it equals the decode definition."""
+    rng = np.random.default_rng(29)
+    page, hq, hkv, d = 4, 4, 2, 3
+    nks = [9, 1, 12, 4]
+    nqs = [3, 1, 12, 0]
+    pages = [-(-n // page) for n in nks]
+    P = sum(pages)
+    perm = rng.permutation(P)
+    table = np.zeros((len(nks), max(pages)), dtype=np.int64)
+    off = 0
+    for b, n in enumerate(pages):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    kc = rng.standard_normal((P, page, hkv, d))
+    vc = rng.standard_normal((P, page, hkv, d))
+    cq = np.concatenate([[0], np.cumsum(nqs)])
+    ck = np.concatenate([[0], np.cumsum(nks)])
+    q = rng.standard_normal((int(cq[-1]), hq, d))
+    kflat = np.concatenate([OA.paged_gather(kc, table[b], nks[b]) for b in range(len(nks))])
+    vflat = np.concatenate([OA.paged_gather(vc, table[b], nks[b]) for b in range(len(nks))])
+    for window in [(-1, -1), (2, -1), (1, 1)]:
+        for causal in (True, False):
+            a = OA.paged_prefill_ref(q, kc, vc, table, cq, nks, causal=causal, softmax_scale=0.6,
+                                     window=window)
+            b = OA.attention_ref(q, kflat, vflat, causal=causal, softmax_scale=0.6, cu_seqlens_q=cq,
+                                 cu_seqlens_k=ck, window=window)
+            assert np.max(np.abs(a[0] - b[0])) < 1e-12
+            assert np.array_equal(np.isneginf(a[1]), np.isneginf(b[1]))
+            fin = np.isfinite(b[1])
+            assert np.max(np.abs(a[1][fin] - b[1][fin])) < 1e-12
+    q1 = rng.standard_normal((len(nks), hq, d))
+    a = OA.paged_prefill_ref(q1, kc, vc, table, np.arange(len(nks) + 1), nks, causal=True,
+                             softmax_scale=0.6)
+    o, l = OA.decode_ref(q1, kc, vc, table, nks, softmax_scale=0.6)
+    assert np.max(np.abs(a[0] - o)) < 1e-12 and np.max(np.abs(a[1].T - l)) < 1e-12
+
+
 # ---- gradients ----------------------------------------------------------------
 
 def check_bwd_sdpa_fp64():
@@ -536,5 +651,5 @@ ALL_CHECKS = [
     check_brute_force, check_sdpa_fp64, check_paged, check_split_combine,
     check_numpy_tiled_exactness, check_varlen_packing, check_rows_api,
     check_bwd_sdpa_fp64, check_bwd_finite_differences, check_bwd_identities,
-    check_bwd_gqa_and_packing,
+    check_bwd_gqa_and_packing, check_window_forms, check_window_brute_force, check_paged_prefill,
 ]

@@ -110,7 +110,33 @@ def _bwd_group_not_summed(q, k, v, dout, **kw):
     return dq, dk, dv
 
 
+_orig_window = OA.window_keep
+
+
+def _window_left_off_by_one(nq, nk, left, right):
+    keep = _orig_window(nq, nk, left, right)
+    if left >= 0:
+        i = np.arange(nq)[:, None]
+        j = np.arange(nk)[None, :]
+        keep &= j > i + (nk - nq) - left
+    return keep
+
+
+def _window_top_left(nq, nk, left, right):
+    i = np.arange(nq)[:, None]
+    j = np.arange(nk)[None, :]
+    keep = np.ones((nq, nk), dtype=bool)
+    if left >= 0:
+        keep &= j >= i - left
+    if right >= 0:
+        keep &= j <= i + right
+    return keep
+
+
 MUTANTS = {
+    "window_left_off_by_one": ("window_keep", _window_left_off_by_one),
+    "window_sides_swapped": ("window_keep", lambda nq, nk, l, r: _orig_window(nq, nk, r, l)),
+    "window_top_left": ("window_keep", _window_top_left),
     "bwd_no_rowsum_term": ("_attend_rows_bwd", _bwd_no_rowsum),
     "bwd_rowsum_of_dp": ("_attend_rows_bwd", _bwd_rowsum_of_dp),
     "bwd_dq_scale_dropped": ("_attend_rows_bwd", lambda Q, K, V, G, s, keep: (lambda a, b, c: (a / s, b, c))(*_orig_bwd_rows(Q, K, V, G, s, keep))),
