@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = [
-    "AttnError", "lib", "lib_path", "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+    "AttnError", "lib", "lib_path", "attn_fwd", "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_bytes",
     "attn_decode_splitkv", "attn_decode_combine",
     "attn_decode", "attn_decode_num_splits", "attn_decode_default_chunk",
     "attn_decode_workspace_bytes", "attn_check_cu_seqlens", "attn_check_block_table",
@@ -44,6 +44,8 @@ _SIGNATURES = {
     "attn_status_str": ([_I], ctypes.c_char_p),
     "attn_last_error": ([], ctypes.c_char_p),
     "attn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "attn_fwd_ex": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                     _P, _P, _P], _I),
     "attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                   _P, _P, _P, _P, ctypes.c_size_t, _P], _I),
     "attn_bwd_workspace_bytes": ([_I, _I], ctypes.c_size_t),
@@ -113,12 +115,13 @@ def _need(t, name, dtype, device=None):
 
 def attn_fwd(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=None,
              max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None, return_lse=True,
-             stream=None):
+             window=(-1, -1), stream=None):
     """Forward pass; returns (out, lse) (lse is None when return_lse is False).
 
     Dense: q [B, Nq, Hq, d], k/v [B, Nk, Hkv, d] -> out like q, lse [B, Hq, Nq].
     Packed: q [TQ, Hq, d], k/v [TK, Hkv, d] with int32 cu_seqlens_q/k [B + 1]
     and max_seqlen_q/k -> out like q, lse [Hq, TQ].
+    window: (left, right) local window, -1 for an unbounded side.
     """
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -167,10 +170,55 @@ def attn_fwd(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=
         lse = None
     if q.numel() == 0:
         return out, lse
+    wl, wr = (int(x) for x in window)
     with torch.cuda.device(dev):
-        st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                            batch, mq, mk, hq, hkv, d, 1 if causal else 0, float(softmax_scale),
-                            _ptr(out), _ptr(lse), _stream(stream, dev))
+        if wl == -1 and wr == -1:
+            st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                batch, mq, mk, hq, hkv, d, 1 if causal else 0, float(softmax_scale),
+                                _ptr(out), _ptr(lse), _stream(stream, dev))
+        else:
+            st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                   None, None, batch, mq, mk, hq, hkv, d, 256, 0, 0,
+                                   1 if causal else 0, wl, wr, float(softmax_scale), _ptr(out),
+                                   _ptr(lse), _stream(stream, dev))
+    _check(st)
+    return out, lse
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, *, max_seqlen_q,
+                   causal, softmax_scale, window=(-1, -1), out=None, lse=None, stream=None):
+    """Paged prefill: packed new rows q [TQ, Hq, d] (cu_seqlens_q [B + 1]) against
+    caches [P, 256, Hkv, d] through block_table int32 [B, maxp], with seqlens_k
+    int32 [B] cached keys per sequence (including the new rows).
+    Returns (out [TQ, Hq, d], lse [Hq, TQ])."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expects q [TQ,Hq,d] and caches [P,page,Hkv,d]")
+    batch = cu_seqlens_q.numel() - 1
+    if seqlens_k.numel() != batch or block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError("seqlens_k and block_table must have one entry / row per sequence")
+    tq, hq, d = q.shape
+    num_pages, page, hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("q and cache head dims differ")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq, tq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.bfloat16, dev)
+    _need(lse, "lse", torch.float32, dev)
+    if tq == 0:
+        return out, lse
+    wl, wr = (int(x) for x in window)
+    with torch.cuda.device(dev):
+        st = lib().attn_fwd_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), None,
+                               _ptr(block_table), _ptr(seqlens_k), batch, int(max_seqlen_q), 0, hq, hkv,
+                               d, page, block_table.shape[1], num_pages, 1 if causal else 0, wl, wr,
+                               float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream, dev))
     _check(st)
     return out, lse
 

@@ -71,14 +71,26 @@ const char* attn_status_str(int status) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
-attn_status_t attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
-                       const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k,
-                       int num_heads_q, int num_heads_kv, int head_dim, int causal,
-                       float softmax_scale, void* out, float* lse, void* stream) {
+attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, const int32_t* block_table, const int32_t* seqlens_k,
+                          int batch, int max_seqlen_q, int max_seqlen_k, int num_heads_q, int num_heads_kv,
+                          int head_dim, int page_size, int max_pages_per_seq, int num_pages, int causal,
+                          int window_left, int window_right, float softmax_scale, void* out, float* lse,
+                          void* stream) {
     if (!q || !k || !v || !out) return fail(ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
+    const bool paged = block_table != nullptr;
     const bool varlen = cu_seqlens_q != nullptr;
-    if (varlen != (cu_seqlens_k != nullptr))
-        return fail(ATTN_ERR_NULL, "cu_seqlens_q and cu_seqlens_k must both be NULL or both be set");
+    if (paged) {
+        if (!cu_seqlens_q || cu_seqlens_k || !seqlens_k)
+            return fail(ATTN_ERR_NULL, "paged mode needs cu_seqlens_q and seqlens_k, and no cu_seqlens_k");
+        if (page_size != 256) return fail(ATTN_ERR_UNSUPPORTED, "page_size=%d, only 256 is supported", page_size);
+        if (max_pages_per_seq < 1 || num_pages < 1)
+            return fail(ATTN_ERR_SHAPE, "max_pages_per_seq=%d num_pages=%d", max_pages_per_seq, num_pages);
+    } else {
+        if (seqlens_k) return fail(ATTN_ERR_NULL, "seqlens_k is only for paged mode (block_table set)");
+        if (varlen != (cu_seqlens_k != nullptr))
+            return fail(ATTN_ERR_NULL, "cu_seqlens_q and cu_seqlens_k must both be NULL or both be set");
+    }
     if (batch < 1 || max_seqlen_q < 1 || max_seqlen_k < (varlen ? 0 : 1) || num_heads_q < 1 ||
         num_heads_kv < 1)
         return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d max_seqlen_q=%d max_seqlen_k=%d "
@@ -90,10 +102,12 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, const int32_
     if (!head_dim_supported(head_dim))
         return fail(ATTN_ERR_UNSUPPORTED, "head_dim=%d not in {64,128,256}", head_dim);
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1 (got %d)", causal);
+    if (window_left < -1 || window_right < -1)
+        return fail(ATTN_ERR_SHAPE, "window sides must be >= -1 (got %d, %d)", window_left, window_right);
     attn_status_t st = check_scale(softmax_scale);
     if (st != ATTN_OK) return st;
-    // Aliasing: byte ranges are known in dense mode; packed mode knows only
-    // the start pointers on the host.
+    // Aliasing: byte ranges are known in dense mode; packed and paged modes
+    // know only the start pointers on the host.
     if (!varlen) {
         const size_t nq = (size_t)batch * max_seqlen_q, nk = (size_t)batch * max_seqlen_k;
         const size_t qbytes = nq * num_heads_q * head_dim * 2;
@@ -122,8 +136,23 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, const int32_
     p.hq = num_heads_q;
     p.hkv = num_heads_kv;
     p.scale = softmax_scale;
-    return hip_status(attn::launch_fwd(p, head_dim, causal != 0, varlen, static_cast<hipStream_t>(stream)),
+    p.wl = window_left;
+    p.wr = window_right;
+    p.block_table = block_table;
+    p.seqlens_k = seqlens_k;
+    p.max_pages = max_pages_per_seq;
+    p.num_pages = num_pages;
+    return hip_status(attn::launch_fwd(p, head_dim, causal != 0, varlen, paged, static_cast<hipStream_t>(stream)),
                       "attn_fwd launch");
+}
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                       const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k,
+                       int num_heads_q, int num_heads_kv, int head_dim, int causal,
+                       float softmax_scale, void* out, float* lse, void* stream) {
+    return attn_fwd_ex(q, k, v, cu_seqlens_q, cu_seqlens_k, nullptr, nullptr, batch, max_seqlen_q,
+                       max_seqlen_k, num_heads_q, num_heads_kv, head_dim, 256, 0, 0, causal, -1, -1,
+                       softmax_scale, out, lse, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int total_q, int num_heads_q) {

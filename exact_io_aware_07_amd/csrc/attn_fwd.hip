@@ -27,14 +27,19 @@
 
 namespace attn {
 
+// Page size of the paged prefill's cache (as the paged decode).
+constexpr int kFwdPage = 256;
+
 // K fragment reads issued ahead of the first score MFMA of a tile.
 #ifndef ATTN_FWD_K_LEAD
 #define ATTN_FWD_K_LEAD 8
 #endif
 
-template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN>
+template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN, bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdParams p) {
+    static_assert(!PAGED || VARLEN, "paged prefill packs its queries");
+    static_assert(kFwdPage % BC == 0, "key tiles must not straddle pages");
     constexpr int NT = NW * 64;
     constexpr int ROWS_W = 32 * QB;
     constexpr int BR = NW * ROWS_W;
@@ -94,8 +99,22 @@ void attn_fwd_kernel(FwdParams p) {
     }
     const int kvh = hq / (p.hq / p.hkv);
 
-    int q_off, k_off, Nq, Nk;
-    if constexpr (VARLEN) {
+    int q_off, k_off = 0, Nq, Nk;
+    bool bad = false;  // paged: a page id out of range, or more keys than the table holds
+    if constexpr (PAGED) {
+        q_off = p.cu_q[b];
+        Nq = p.cu_q[b + 1] - q_off;
+        Nq = Nq < 0 ? 0 : Nq;
+        Nk = p.seqlens_k[b];
+        if (Nk < 0) {
+            Nk = 0;
+            bad = true;
+        }
+        if ((long)Nk > (long)p.max_pages * kFwdPage) {
+            Nk = p.max_pages * kFwdPage;
+            bad = true;
+        }
+    } else if constexpr (VARLEN) {
         q_off = p.cu_q[b];
         Nq = p.cu_q[b + 1] - q_off;
         k_off = p.cu_k[b];
@@ -111,24 +130,59 @@ void attn_fwd_kernel(FwdParams p) {
     const int q0 = qt * BR;
     if (q0 >= Nq) return;
 
-    // K/V tile range: tile t covers keys [t*BC, t*BC + BC).
-    int n_tiles = (Nk + BC - 1) / BC;
-    if constexpr (CAUSAL) {
-        const int last_row = min(q0 + BR, Nq) - 1;
-        const int kmax = last_row + Nk - Nq;  // last key any row of the tile may see
-        n_tiles = kmax < 0 ? 0 : min(n_tiles, kmax / BC + 1);
-    }
+    // Row i (of its sequence) sees keys lo(i) .. hi(i): the bottom-right
+    // causal rule and the local window (keys i + Nk - Nq - left .. i + Nk -
+    // Nq + right, -1 unbounded; "Deep Dive - FlashAttention", "Causal 2.1 is
+    // the decode gotcha"), clipped to the keys that exist.
+    const long shift = (long)Nk - Nq;
+    long roff = CAUSAL ? 0 : (1L << 40);
+    if (p.wr >= 0 && p.wr < roff) roff = p.wr;
+    const long loff = p.wl >= 0 ? p.wl : (1L << 40);
+    auto hi_of = [&](int i) __attribute__((always_inline)) {
+        const long h = i + shift + roff;
+        return (int)(h < Nk - 1 ? h : Nk - 1);
+    };
+    auto lo_of = [&](int i) __attribute__((always_inline)) {
+        const long l = i + shift - loff;
+        return (int)(l > 0 ? l : 0);
+    };
+    // K/V tile range: tile t covers keys [t*BC, t*BC + BC); tiles wholly
+    // outside every row's range are never visited.
+    const int last_row = min(q0 + BR, Nq) - 1;
+    const int t_lo = lo_of(q0) / BC;
+    int t_end = hi_of(last_row) < 0 ? 0 : hi_of(last_row) / BC + 1;
+    if (t_end < t_lo) t_end = t_lo;
 
     const long kv_stride = (long)p.hkv * D;
     const uint32_t stride_b = (uint32_t)(kv_stride * 2);
     const uint16_t* kbase = p.k + ((long)k_off * p.hkv + kvh) * D;
     const uint16_t* vbase = p.v + ((long)k_off * p.hkv + kvh) * D;
 
-    // This wave's rows and their key horizon.
+    // This wave's rows and the key ranges of its first and last row.
     const int wr0 = q0 + wave * ROWS_W;
     const bool wave_rows = wr0 < Nq;
-    const int w_last_key = min(wr0 + ROWS_W, Nq) - 1 + Nk - Nq;  // causal: last key the wave sees
-    const int w_first_key_lim = wr0 + Nk - Nq;                    // causal: first row's last key
+    const int w_last_row = min(wr0 + ROWS_W, Nq) - 1;
+    const int w_hi_max = hi_of(w_last_row), w_hi_min = hi_of(wr0);
+    const int w_lo_min = lo_of(wr0), w_lo_max = lo_of(w_last_row);
+
+    // Loads of key tile t: contiguous K/V, or the page the block table names.
+    auto issue_tile = [&](int t, uint32_t st) __attribute__((always_inline)) {
+        const int key0 = t * BC;
+        if constexpr (PAGED) {
+            const int phys = p.block_table[(long)b * p.max_pages + key0 / kFwdPage];
+            if (phys < 0 || phys >= p.num_pages) {
+                bad = true;
+                Tile::issue(p.k, p.v, stride_b, 0, st, wave, lane);
+            } else {
+                const long row0 = (long)phys * kFwdPage + key0 % kFwdPage;
+                Tile::issue(p.k + (row0 * p.hkv + kvh) * D, p.v + (row0 * p.hkv + kvh) * D, stride_b,
+                            Nk - key0, st, wave, lane);
+            }
+        } else {
+            const long off = (long)key0 * kv_stride;
+            Tile::issue(kbase + off, vbase + off, stride_b, Nk - key0, st, wave, lane);
+        }
+    };
 
     // Q^T fragments (B operand), resident for the whole loop.
     u32x4 qf[QB][KS];
@@ -159,19 +213,16 @@ void attn_fwd_kernel(FwdParams p) {
     }
     const float c2 = p.scale * kLog2e;
 
-    if (n_tiles > 0) Tile::issue(kbase, vbase, stride_b, Nk, lds_addr(stage0), wave, lane);
+    if (t_end > t_lo) issue_tile(t_lo, lds_addr(stage0));
     wait_vmem();
     __syncthreads();
 
     auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
         const char* ks = cur;
         const char* vs = cur + Tile::K_BYTES;
-        if (t + 1 < n_tiles) {
-            const long off = (long)(t + 1) * BC * kv_stride;
-            Tile::issue(kbase + off, vbase + off, stride_b, Nk - (t + 1) * BC, lds_addr(nxt), wave, lane);
-        }
+        if (t + 1 < t_end) issue_tile(t + 1, lds_addr(nxt));
         const int k0 = t * BC;
-        const bool active = wave_rows && (!CAUSAL || k0 <= w_last_key);
+        const bool active = wave_rows && k0 <= w_hi_max && k0 + BC - 1 >= w_lo_min;
         if (active) {
             // ---- S^T = K Q^T --------------------------------------------
             f32x16 sacc[KB][QB];
@@ -200,18 +251,19 @@ void attn_fwd_kernel(FwdParams p) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, QB * ATTN_FWD_K_LEAD, 0);
             // ---- mask: only tiles crossing the diagonal or the key end ----
-            const bool need_mask =
-                (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > w_first_key_lim);
+            const bool need_mask = (k0 + BC - 1 > w_hi_min) || (k0 < w_lo_max);
             if (need_mask) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     const int row = wr0 + 32 * qb + l32;
-                    const int lim = CAUSAL ? min(Nk - 1, row + Nk - Nq) : Nk - 1;
+                    const int hi = hi_of(row), lo = lo_of(row);
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (k0 + score_key(kb, r, lane) > lim) sacc[kb][qb][r] = -INFINITY;
+                        for (int r = 0; r < 16; ++r) {
+                            const int j = k0 + score_key(kb, r, lane);
+                            if (j > hi || j < lo) sacc[kb][qb][r] = -INFINITY;
+                        }
                 }
             }
             // ---- online softmax --------------------------------------------
@@ -274,9 +326,9 @@ void attn_fwd_kernel(FwdParams p) {
         wait_vmem();
         __syncthreads();
     };
-    for (int t = 0; t < n_tiles; t += 2) {
+    for (int t = t_lo; t < t_end; t += 2) {
         step(t, stage0, stage1);
-        if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
+        if (t + 1 < t_end) step(t + 1, stage1, stage0);
     }
 
     // ---- epilogue: out = O / l (bf16, round to nearest even), lse in nats ----
@@ -287,7 +339,7 @@ void attn_fwd_kernel(FwdParams p) {
         const int row = wr0 + 32 * qb + l32;
         const float l_tot = pair_sum(l_part[qb]);
         if (row < Nq) {
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            const float inv = bad ? NAN : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
             uint16_t* orow = p.out + ((long)(q_off + row) * p.hq + hq) * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -298,7 +350,7 @@ void attn_fwd_kernel(FwdParams p) {
                     *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * h) = w;
                 }
             if (p.lse != nullptr && h == 0) {
-                const float lse = l_tot > 0.0f ? (m_run[qb] + __log2f(l_tot)) * kLn2 : -INFINITY;
+                const float lse = bad ? NAN : (l_tot > 0.0f ? (m_run[qb] + __log2f(l_tot)) * kLn2 : -INFINITY);
                 if constexpr (VARLEN)
                     p.lse[(long)hq * total_q + q_off + row] = lse;
                 else
@@ -308,7 +360,7 @@ void attn_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN>
+template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN, bool PAGED>
 static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     FwdParams p = p0;
     constexpr int BR = NW * 32 * QB;
@@ -316,19 +368,23 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     const long grid = (long)p.n_qtiles * p.batch * p.hq;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, WPE, CAUSAL, VARLEN>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, WPE, CAUSAL, VARLEN, PAGED>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D, int QB, int BC, int NW, int WPE>
-static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, hipStream_t s) {
-    if (causal) {
-        return varlen ? launch_fwd_cfg<D, QB, BC, NW, WPE, true, true>(p, s)
-                      : launch_fwd_cfg<D, QB, BC, NW, WPE, true, false>(p, s);
+static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, bool paged, hipStream_t s) {
+    if (paged) {
+        return causal ? launch_fwd_cfg<D, QB, BC, NW, WPE, true, true, true>(p, s)
+                      : launch_fwd_cfg<D, QB, BC, NW, WPE, false, true, true>(p, s);
     }
-    return varlen ? launch_fwd_cfg<D, QB, BC, NW, WPE, false, true>(p, s)
-                  : launch_fwd_cfg<D, QB, BC, NW, WPE, false, false>(p, s);
+    if (causal) {
+        return varlen ? launch_fwd_cfg<D, QB, BC, NW, WPE, true, true, false>(p, s)
+                      : launch_fwd_cfg<D, QB, BC, NW, WPE, true, false, false>(p, s);
+    }
+    return varlen ? launch_fwd_cfg<D, QB, BC, NW, WPE, false, true, false>(p, s)
+                  : launch_fwd_cfg<D, QB, BC, NW, WPE, false, false, false>(p, s);
 }
 
 // Tile shapes per head dim: <QB (32-row blocks per wave), BC (keys per tile),
@@ -343,11 +399,11 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, hip
 #define ATTN_FWD256_CFG 1, 32, 4, 1
 #endif
 
-hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s) {
+hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, bool paged, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_fwd_d<64, ATTN_FWD64_CFG>(p, causal, varlen, s);
-        case 128: return launch_fwd_d<128, ATTN_FWD128_CFG>(p, causal, varlen, s);
-        case 256: return launch_fwd_d<256, ATTN_FWD256_CFG>(p, causal, varlen, s);
+        case 64: return launch_fwd_d<64, ATTN_FWD64_CFG>(p, causal, varlen, paged, s);
+        case 128: return launch_fwd_d<128, ATTN_FWD128_CFG>(p, causal, varlen, paged, s);
+        case 256: return launch_fwd_d<256, ATTN_FWD256_CFG>(p, causal, varlen, paged, s);
         default: return hipErrorInvalidValue;
     }
 }

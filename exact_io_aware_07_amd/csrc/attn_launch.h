@@ -17,6 +17,11 @@ struct FwdParams {
     int batch, max_q, max_k, hq, hkv;
     int n_qtiles;  // filled in by the launcher
     float scale;
+    int wl = -1, wr = -1;  // local window (left, right); -1: unbounded side
+    // Paged prefill: k and v are [num_pages, 256, hkv, d] caches.
+    const int32_t* block_table = nullptr;
+    const int32_t* seqlens_k = nullptr;
+    int max_pages = 0, num_pages = 0;
 };
 
 struct DecodeParams {
@@ -59,7 +64,7 @@ struct BwdParams {
     float scale;
 };
 
-hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, bool paged, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_decode_combine(const CombineParams& p, int head_dim, hipStream_t s);

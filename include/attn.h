@@ -102,6 +102,43 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v,
                        void* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_ex -- attn_fwd with a local window and an optional paged K/V cache.
+ *
+ * Local window ("Deep Dive - FlashAttention", "Causal 2.1 is the decode
+ * gotcha"): query row i of a sequence with Nq queries and Nk keys sees key j
+ * when i + Nk - Nq - window_left <= j <= i + Nk - Nq + window_right; a side
+ * of -1 is unbounded, and causal = 1 further restricts the right side to
+ * j <= i + Nk - Nq.  window_left = window_right = -1 is attn_fwd.  Rows that
+ * see no key get out = 0 and lse = -inf.  Key tiles outside every row's
+ * window are not read.
+ *
+ * Paged prefill (block_table non-NULL): new query rows against a paged cache
+ * that already holds their keys ("Deep Dive - FlashAttention", "Paged KV is
+ * a lookup, not a cache manager"; "FlashAttention-3 and PagedAttention:
+ * IO-Aware Attention Kernels (2026)", "Block tables and what the kernel
+ * does").  k, v are k_cache, v_cache [num_pages, page_size, num_heads_kv,
+ * head_dim] bf16; block_table int32 [batch, max_pages_per_seq]; seqlens_k
+ * int32 [batch] device array of cached keys per sequence (the last Nq of
+ * which belong to the sequence's new rows, so masks align bottom-right);
+ * queries are packed: cu_seqlens_q required, cu_seqlens_k must be NULL; out
+ * [TQ, Hq, d], lse [Hq, TQ].  page_size must be 256.  A page id outside
+ * [0, num_pages) in a tile a workgroup reads, or a length beyond
+ * max_pages_per_seq * page_size, turns that workgroup's rows into NaN (never
+ * a fault); cache rows past seqlens_k are never used.
+ * Without block_table, seqlens_k must be NULL and the other arguments are as
+ * in attn_fwd (page_size, max_pages_per_seq and num_pages are ignored).
+ * window_left, window_right >= -1, else ATTN_ERR_SHAPE.
+ */
+attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* block_table, const int32_t* seqlens_k,
+                          int batch, int max_seqlen_q, int max_seqlen_k,
+                          int num_heads_q, int num_heads_kv, int head_dim,
+                          int page_size, int max_pages_per_seq, int num_pages,
+                          int causal, int window_left, int window_right, float softmax_scale,
+                          void* out, float* lse, void* stream);
+
+/*
  * attn_bwd -- gradients of attn_fwd by recomputation.
  *
  * From the forward's saved q, k, v, out and lse and the upstream gradient

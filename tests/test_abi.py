@@ -102,6 +102,30 @@ def test_decode_combine_rejects(kw, code):
     assert comb(**kw) == code
 
 
+def fwd_ex(**kw):
+    a = dict(q=FAKE, k=FAKE2, v=FAKE3, cq=NULL, ck=NULL, bt=NULL, sk=NULL, batch=1, mq=8, mk=8, hq=4,
+             hkv=2, d=128, page=256, maxp=4, npages=8, causal=1, wl=-1, wr=-1, scale=0.125, out=OUT,
+             lse=LSE)
+    a.update(kw)
+    return ea.lib().attn_fwd_ex(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["bt"], a["sk"], a["batch"],
+                                a["mq"], a["mk"], a["hq"], a["hkv"], a["d"], a["page"], a["maxp"],
+                                a["npages"], a["causal"], a["wl"], a["wr"], a["scale"], a["out"], a["lse"],
+                                None)
+
+
+PAGED = dict(bt=FAKE, cq=FAKE2, sk=FAKE3, k=ctypes.c_void_p(0x11000), v=ctypes.c_void_p(0x12000))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wl=-2), 2), (dict(wr=-5), 2), (dict(sk=FAKE), 1), (dict(q=NULL), 1), (dict(d=96), 3),
+    (dict(PAGED, cq=NULL), 1), (dict(PAGED, sk=NULL), 1), (dict(PAGED, ck=FAKE), 1),
+    (dict(PAGED, page=128), 3), (dict(PAGED, maxp=0), 2), (dict(PAGED, npages=0), 2),
+    (dict(PAGED, wl=-3), 2), (dict(PAGED, out=FAKE2), 5),
+])
+def test_fwd_ex_rejects(kw, code):
+    assert fwd_ex(**kw) == code
+
+
 DQ = ctypes.c_void_p(0x60000000)
 DK = ctypes.c_void_p(0x70000000)
 DV = ctypes.c_void_p(0x78000000)
