@@ -120,7 +120,7 @@ PAGED = dict(bt=FAKE, cq=FAKE2, sk=FAKE3, k=ctypes.c_void_p(0x11000), v=ctypes.c
     (dict(wl=-2), 2), (dict(wr=-5), 2), (dict(sk=FAKE), 1), (dict(q=NULL), 1), (dict(d=96), 3),
     (dict(PAGED, cq=NULL), 1), (dict(PAGED, sk=NULL), 1), (dict(PAGED, ck=FAKE), 1),
     (dict(PAGED, page=128), 3), (dict(PAGED, maxp=0), 2), (dict(PAGED, npages=0), 2),
-    (dict(PAGED, wl=-3), 2), (dict(PAGED, out=FAKE2), 5),
+    (dict(PAGED, wl=-3), 2), (dict(PAGED, out=FAKE), 5),
 ])
 def test_fwd_ex_rejects(kw, code):
     assert fwd_ex(**kw) == code
