@@ -165,11 +165,16 @@ void attn_fwd_kernel(FwdParams p) {
     const int w_hi_max = hi_of(w_last_row), w_hi_min = hi_of(wr0);
     const int w_lo_min = lo_of(wr0), w_lo_max = lo_of(w_last_row);
 
+    // Page id of key tile t (paged mode).  It is read one step before the
+    // tile's loads are issued, so the table lookup never delays them.
+    auto page_of = [&](int t) __attribute__((always_inline)) {
+        return PAGED ? p.block_table[(long)b * p.max_pages + (t * BC) / kFwdPage] : 0;
+    };
     // Loads of key tile t: contiguous K/V, or the page the block table names.
-    auto issue_tile = [&](int t, uint32_t st) __attribute__((always_inline)) {
+    auto issue_tile = [&](int t, int phys_v, uint32_t st) __attribute__((always_inline)) {
         const int key0 = t * BC;
         if constexpr (PAGED) {
-            const int phys = p.block_table[(long)b * p.max_pages + key0 / kFwdPage];
+            const int phys = __builtin_amdgcn_readfirstlane(phys_v);
             if (phys < 0 || phys >= p.num_pages) {
                 bad = true;
                 Tile::issue(p.k, p.v, stride_b, 0, st, wave, lane);
@@ -213,14 +218,21 @@ void attn_fwd_kernel(FwdParams p) {
     }
     const float c2 = p.scale * kLog2e;
 
-    if (t_end > t_lo) issue_tile(t_lo, lds_addr(stage0));
+    int phys_next = 0;  // page id of the next tile to issue (paged mode)
+    if (t_end > t_lo) {
+        issue_tile(t_lo, page_of(t_lo), lds_addr(stage0));
+        if (t_lo + 1 < t_end) phys_next = page_of(t_lo + 1);
+    }
     wait_vmem();
     __syncthreads();
 
     auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
         const char* ks = cur;
         const char* vs = cur + Tile::K_BYTES;
-        if (t + 1 < t_end) issue_tile(t + 1, lds_addr(nxt));
+        if (t + 1 < t_end) {
+            issue_tile(t + 1, phys_next, lds_addr(nxt));
+            if (PAGED && t + 2 < t_end) phys_next = page_of(t + 2);
+        }
         const int k0 = t * BC;
         const bool active = wave_rows && k0 <= w_hi_max && k0 + BC - 1 >= w_lo_min;
         if (active) {
