@@ -10,16 +10,20 @@ Sources (page title, section):
     "Two tiles by hand", "The public interface is several kernels",
     "Backward recomputes tiles on purpose" (the gradients), "Causal 2.1 is the
     decode gotcha" (the local window),
-    "Causal 2.1 is the decode gotcha", "Paged KV is a lookup, not a cache manager".
+    "Paged KV is a lookup, not a cache manager" (also the in-place cache append).
   * "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)":
     "Runnable Example: Measuring the IO Gap", "Decode-Time Kernels".
   * "Flash Attention: A Complete Architectural Autopsy": "Part 1".
-  * "FlashAttention: Part 1": sections 2.2, 3.5, 4.1.
+  * "FlashAttention: Part 1": sections 2.2, 3.5, 4.1, 4.2 (rotary embedding as a
+    transform of Q and K before attention; module kvcache).
 
 Parity status: every function here is pinned by the tests in
 tests/test_oracle_pins.py except two conventions the pages leave open (the
 lse of a row with no allowed key, and the packed [Hq, total_q] lse layout of
-variable-length batches); those two are "parity unpinned".
+variable-length batches); those two are "parity unpinned".  The rotary
+formula and the bf16 rounding of rotated rows are readings (the pages give
+neither); they are pinned to hand-worked turns, RoFormer's relative-position
+property and PyTorch's float32 -> bfloat16 conversion.
 """
 from .attention import (  # noqa: F401
     kv_head_for_queries,
@@ -31,4 +35,10 @@ from .attention import (  # noqa: F401
     attention_bwd_ref,
     window_keep,
     paged_prefill_ref,
+)
+from .kvcache import (  # noqa: F401
+    round_bf16,
+    rotary_ref,
+    append_ref,
+    decode_append_ref,
 )

@@ -11,6 +11,7 @@ import os
 import numpy as np
 
 import oracle.attention as OA
+import oracle.kvcache as OK
 from brute_force import brute_attention
 from tiled_recurrence import combine_partials, tiled_attention, tiled_row
 
@@ -645,6 +646,155 @@ def check_bwd_gqa_and_packing():
     assert np.max(np.abs(sub[0][:, 2:] - dq[:, 2:])) < 1e-12 and np.all(sub[0][:, :2] == 0)
 
 
+# ---- cache append and rotary ----------------------------------------------------
+
+
+def check_round_bf16():
+    """round_bf16 equals PyTorch's float32 -> bfloat16 conversion (round to
+    nearest, ties to even) on float32 inputs, exact ties included, and the
+    hand cases: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 and goes to 1;
+    1 + 3 * 2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6 and goes to
+    1 + 2^-6; the sign is kept; bf16 values are fixed points."""
+    import torch
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(4000), rng.standard_normal(300) * 1e-30,
+                        rng.standard_normal(300) * 1e30]).astype(np.float32)
+    bits = x.view(np.uint32)
+    ties = ((bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties, (bits & np.uint32(0xFFFF0000)).view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(OK.round_bf16(x.astype(np.float64)), ref)
+    hand = [(1 + 2 ** -8, 1.0), (1 + 3 * 2 ** -8, 1 + 2 ** -6), (-(1 + 2 ** -8), -1.0),
+            (1 + 2 ** -8 + 2 ** -20, 1 + 2 ** -7), (0.0, 0.0), (2.0 ** -100, 2.0 ** -100)]
+    for a, b in hand:
+        assert OK.round_bf16(np.array([a]))[0] == b, (a, b)
+
+
+def _rope_tables(max_pos, rotary_dim, base=10000.0):
+    """RoFormer's angles: pair i turns by p * base^(-2i / rotary_dim) at position p."""
+    theta = base ** (-2.0 * np.arange(rotary_dim // 2) / rotary_dim)
+    ang = np.arange(max_pos)[:, None] * theta[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def check_rotary_quarter_turns():
+    """Quarter and half turns worked by hand.  At position 1 the two pairs turn
+    by 90 and 180 degrees (cos = [0, -1], sin = [1, 0]); x = [1, 2, 3, 4]
+    becomes [-3, -2, 1, -4] when the pairs are the halves (1, 3), (2, 4) and
+    [-2, 1, -3, -4] when they are neighbours (1, 2), (3, 4).  Position 0
+    (cos 1, sin 0) leaves x alone.  With rotary_dim = 2 only the first two
+    features turn: [-2, 1, 3, 4]."""
+    cos = np.array([[1.0, 1.0], [0.0, -1.0]])
+    sin = np.array([[0.0, 0.0], [1.0, 0.0]])
+    x = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    rot = lambda pos, **kw: OK.rotary_ref(x, cos, sin, [pos], **kw)[0, 0].tolist()
+    assert rot(1, rotary_dim=4, interleaved=False) == [-3.0, -2.0, 1.0, -4.0]
+    assert rot(1, rotary_dim=4, interleaved=True) == [-2.0, 1.0, -3.0, -4.0]
+    assert rot(0, rotary_dim=4, interleaved=False) == [1.0, 2.0, 3.0, 4.0]
+    assert rot(0, rotary_dim=4, interleaved=True) == [1.0, 2.0, 3.0, 4.0]
+    one = OK.rotary_ref(x, cos[:, :1], sin[:, :1], [1], rotary_dim=2, interleaved=False)
+    assert one[0, 0].tolist() == [-2.0, 1.0, 3.0, 4.0]
+    assert OK.rotary_ref(x, None, None, [5], rotary_dim=0, interleaved=False).tolist() == x.tolist()
+
+
+def check_rotary_relative_position():
+    """With RoFormer's angles the score between a rotated query and a rotated
+    key depends only on the difference of their positions, every row keeps
+    its length, and turning a row and then its negative angle restores it."""
+    rng = np.random.default_rng(13)
+    r, d = 8, 10
+    cos, sin = _rope_tables(80, r)
+    q = rng.standard_normal((1, 3, d))
+    k = rng.standard_normal((1, 3, d))
+    for inter in (False, True):
+        rot = lambda x, p: OK.rotary_ref(x, cos, sin, [p], rotary_dim=r, interleaved=inter)
+        for pq, pk, t in [(5, 3, 7), (20, 20, 11), (0, 9, 30), (40, 1, 25)]:
+            a = np.sum(rot(q, pq) * rot(k, pk), axis=-1)
+            b = np.sum(rot(q, pq + t) * rot(k, pk + t), axis=-1)
+            assert np.max(np.abs(a - b)) < 1e-12
+            assert np.max(np.abs(np.linalg.norm(rot(q, pq), axis=-1) - np.linalg.norm(q, axis=-1))) < 1e-12
+        back = OK.rotary_ref(rot(q, 17), cos[17:18], -sin[17:18], [0], rotary_dim=r, interleaved=inter)
+        assert np.max(np.abs(back - q)) < 1e-12
+
+
+def _append_case(seed=19):
+    rng = np.random.default_rng(seed)
+    page, hq, hkv, d, r = 4, 4, 2, 6, 4
+    lens = [0, 5, 8, 3]
+    need = [-(-(n + 1) // page) for n in lens]
+    P = sum(need) + 2
+    perm = rng.permutation(P)
+    table = np.zeros((len(lens), max(need)), dtype=np.int64)
+    off = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    ang = rng.uniform(-np.pi, np.pi, size=(12, r // 2))
+    return dict(page=page, hq=hq, hkv=hkv, d=d, r=r, lens=lens, table=table,
+                kc=rng.standard_normal((P, page, hkv, d)), vc=rng.standard_normal((P, page, hkv, d)),
+                q=rng.standard_normal((len(lens), hq, d)), kn=rng.standard_normal((len(lens), hkv, d)),
+                vn=rng.standard_normal((len(lens), hkv, d)), cos=np.cos(ang), sin=np.sin(ang))
+
+
+def check_append():
+    """The append adds exactly the new row to each request's keys: after it,
+    the first p + 1 gathered rows are the p rows from before followed by the
+    new key (rotated at p, rounded to bf16) and the new value; no other cache
+    row changes."""
+    c = _append_case()
+    for inter in (False, True):
+        kw = dict(rotary_cos=c["cos"], rotary_sin=c["sin"], rotary_dim=c["r"], interleaved=inter)
+        kc, vc = OK.append_ref(c["kn"], c["vn"], c["kc"], c["vc"], c["table"], c["lens"], **kw)
+        k_rot = OK.round_bf16(OK.rotary_ref(c["kn"], c["cos"], c["sin"], c["lens"], rotary_dim=c["r"],
+                                            interleaved=inter))
+        changed = np.zeros(kc.shape[:3], dtype=bool)
+        for b, p in enumerate(c["lens"]):
+            row = [int(x) for x in c["table"][b]]
+            before_k = OA.paged_gather(c["kc"], row, p)
+            before_v = OA.paged_gather(c["vc"], row, p)
+            after_k = OA.paged_gather(kc, row, p + 1)
+            after_v = OA.paged_gather(vc, row, p + 1)
+            assert np.array_equal(after_k[:p], before_k) and np.array_equal(after_v[:p], before_v)
+            assert np.array_equal(after_k[p], k_rot[b]) and np.array_equal(after_v[p], c["vn"][b])
+            changed[row[p // c["page"]], p % c["page"]] = True
+        assert np.array_equal(kc[~changed], c["kc"][~changed])
+        assert np.array_equal(vc[~changed], c["vc"][~changed])
+
+
+def check_decode_append():
+    """Decode after the append against the scalar loops over the gathered keys
+    plus the new one, with the rotated, bf16-rounded query; a request with no
+    cached key returns its new value row exactly; and the result equals
+    decode_ref over append_ref's caches with lengths p + 1."""
+    c = _append_case(23)
+    for inter in (False, True):
+        kw = dict(rotary_cos=c["cos"], rotary_sin=c["sin"], rotary_dim=c["r"], interleaved=inter)
+        out, lse, q_rot = OK.decode_append_ref(c["q"], c["kn"], c["vn"], c["kc"], c["vc"], c["table"],
+                                               c["lens"], softmax_scale=0.45, **kw)
+        rot = lambda x: OK.round_bf16(OK.rotary_ref(x, c["cos"], c["sin"], c["lens"], rotary_dim=c["r"],
+                                                    interleaved=inter))
+        assert np.array_equal(q_rot, rot(c["q"]))
+        k_rot = rot(c["kn"])
+        for b, p in enumerate(c["lens"]):
+            row = [int(x) for x in c["table"][b]]
+            keys = np.concatenate([OA.paged_gather(c["kc"], row, p), k_rot[b][None]])
+            vals = np.concatenate([OA.paged_gather(c["vc"], row, p), c["vn"][b][None]])
+            bo, bl = brute_attention([q_rot[b][None].tolist()], [keys.tolist()], [vals.tolist()],
+                                     causal=False, scale=0.45)
+            bo = np.array([bo[(0, 0, h)] for h in range(c["hq"])])
+            bl = np.array([bl[(0, 0, h)] for h in range(c["hq"])])
+            assert np.max(np.abs(bo - out[b])) < 1e-12 and np.max(np.abs(bl - lse[b])) < 1e-12
+        grp = c["hq"] // c["hkv"]
+        assert np.array_equal(out[0], np.repeat(c["vn"][0], grp, axis=0))
+        kc, vc = OK.append_ref(c["kn"], c["vn"], c["kc"], c["vc"], c["table"], c["lens"], **kw)
+        o2, l2 = OA.decode_ref(q_rot, kc, vc, c["table"], [p + 1 for p in c["lens"]], softmax_scale=0.45)
+        assert np.max(np.abs(o2 - out)) < 1e-12 and np.max(np.abs(l2 - lse)) < 1e-12
+    # without rotary the query and key pass through (rounded to bf16)
+    out, lse, q_rot = OK.decode_append_ref(c["q"], c["kn"], c["vn"], c["kc"], c["vc"], c["table"], c["lens"],
+                                           softmax_scale=0.45)
+    assert np.array_equal(q_rot, OK.round_bf16(c["q"]))
+
+
 ALL_CHECKS = [
     check_two_tiles_printed, check_tile_states, check_tiles_and_shifts, check_masked_rows,
     check_causal_masks_printed, check_gqa_printed, check_rows_sum_to_one, check_closed_forms,
@@ -652,4 +802,6 @@ ALL_CHECKS = [
     check_numpy_tiled_exactness, check_varlen_packing, check_rows_api,
     check_bwd_sdpa_fp64, check_bwd_finite_differences, check_bwd_identities,
     check_bwd_gqa_and_packing, check_window_forms, check_window_brute_force, check_paged_prefill,
+    check_round_bf16, check_rotary_quarter_turns, check_rotary_relative_position, check_append,
+    check_decode_append,
 ]

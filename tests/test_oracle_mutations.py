@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as OA
+import oracle.kvcache as OK
 import pins
 
 _orig_attend = OA._attend_rows
@@ -164,6 +165,90 @@ MUTANTS = {
 def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(OA, attr, fn)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, f"no pin catches mutant {name}"
+
+
+# ---- cache append and rotary (planted in oracle.kvcache) -------------------------
+
+_orig_rotary = OK.rotary_ref
+_orig_round = OK.round_bf16
+_orig_new_rows = OK._new_rows
+
+
+def _rotary_sign_flipped(x, cos, sin, positions, *, rotary_dim, interleaved):
+    return _orig_rotary(x, cos, None if sin is None else -np.asarray(sin), positions,
+                        rotary_dim=rotary_dim, interleaved=interleaved)
+
+
+def _rotary_pairs_swapped(x, cos, sin, positions, *, rotary_dim, interleaved):
+    return _orig_rotary(x, cos, sin, positions, rotary_dim=rotary_dim, interleaved=not interleaved)
+
+
+def _rotary_position_plus_one(x, cos, sin, positions, *, rotary_dim, interleaved):
+    return _orig_rotary(x, cos, sin, [int(p) + 1 for p in positions], rotary_dim=rotary_dim,
+                        interleaved=interleaved)
+
+
+def _round_truncates(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.where(np.isfinite(x), np.ldexp(np.trunc(m * 256.0) / 256.0, e), x)
+
+
+def _round_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.sign(m) * np.floor(np.abs(m) * 256.0 + 0.5)
+    return np.where(np.isfinite(x), np.ldexp(r / 256.0, e), x)
+
+
+def _query_not_rotated(q, k_new, cos, sin, positions, rotary_dim, interleaved):
+    _, k_rot = _orig_new_rows(q, k_new, cos, sin, positions, rotary_dim, interleaved)
+    return OK.round_bf16(q), k_rot
+
+
+def _append_previous_row(k_new, v_new, k_cache, v_cache, block_table, seqlens_k, **kw):
+    kc, vc = np.array(k_cache, dtype=np.float64), np.array(v_cache, dtype=np.float64)
+    page = kc.shape[1]
+    pos = [int(x) for x in seqlens_k]
+    _, k_rot = OK._new_rows(np.zeros((len(pos), 1, kc.shape[-1])), k_new, kw.get("rotary_cos"),
+                            kw.get("rotary_sin"), pos, kw.get("rotary_dim", 0), kw.get("interleaved", False))
+    for b, p in enumerate(pos):
+        t = max(p - 1, 0)
+        kc[int(block_table[b][t // page]), t % page] = k_rot[b]
+        vc[int(block_table[b][t // page]), t % page] = v_new[b]
+    return kc, vc
+
+
+def _value_not_appended(k_new, v_new, k_cache, v_cache, block_table, seqlens_k, **kw):
+    kc, _ = _orig_append(k_new, v_new, k_cache, v_cache, block_table, seqlens_k, **kw)
+    return kc, np.array(v_cache, dtype=np.float64)
+
+
+_orig_append = OK.append_ref
+
+KV_MUTANTS = {
+    "rotary_sign_flipped": ("rotary_ref", _rotary_sign_flipped),
+    "rotary_pairs_swapped": ("rotary_ref", _rotary_pairs_swapped),
+    "rotary_position_plus_one": ("rotary_ref", _rotary_position_plus_one),
+    "round_truncates": ("round_bf16", _round_truncates),
+    "round_ties_away": ("round_bf16", _round_ties_away),
+    "query_not_rotated": ("_new_rows", _query_not_rotated),
+    "append_previous_row": ("append_ref", _append_previous_row),
+    "value_not_appended": ("append_ref", _value_not_appended),
+}
+
+
+@pytest.mark.parametrize("name", sorted(KV_MUTANTS))
+def test_pins_catch_kvcache_mutant(name, monkeypatch):
+    attr, fn = KV_MUTANTS[name]
+    monkeypatch.setattr(OK, attr, fn)
     caught = []
     for check in pins.ALL_CHECKS:
         try:
