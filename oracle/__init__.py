@@ -23,7 +23,8 @@ lse of a row with no allowed key, and the packed [Hq, total_q] lse layout of
 variable-length batches); those two are "parity unpinned".  The rotary
 formula and the bf16 rounding of rotated rows are readings (the pages give
 neither); they are pinned to hand-worked turns, RoFormer's relative-position
-property and PyTorch's float32 -> bfloat16 conversion.
+property, a hand-worked float32 rounding case with the float64 error bound,
+and PyTorch's float32 -> bfloat16 conversion.
 """
 from .attention import (  # noqa: F401
     kv_head_for_queries,
@@ -39,6 +40,7 @@ from .attention import (  # noqa: F401
 from .kvcache import (  # noqa: F401
     round_bf16,
     rotary_ref,
+    rotary_f32,
     append_ref,
     decode_append_ref,
 )

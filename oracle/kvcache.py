@@ -21,6 +21,11 @@ tables, so the frequencies are the caller's choice.
 Precision (the pages fix none): the cache holds bf16, so the stored key is the
 rotated key rounded to bf16 (round to nearest, ties to even); the rotated query
 is rounded the same way before attention, as any bf16 query input would be.
+Rounding to bf16 picks a stored code, so it is decided in the precision the
+kernel computes the turn in: each product rounded to float32, then the
+difference (or sum) rounded to float32, then that value rounded to bf16
+(rotary_f32).  rotary_ref is the same turn in float64, the mathematical
+definition the float32 one is pinned against.  The attention itself is fp64.
 """
 import numpy as np
 
@@ -66,11 +71,37 @@ def rotary_ref(x, cos, sin, positions, *, rotary_dim, interleaved):
     return out
 
 
+def rotary_f32(x, cos, sin, positions, *, rotary_dim, interleaved):
+    """rotary_ref's turn in float32 arithmetic, as float64 values.
+
+    Each product a*cos, b*sin, a*sin, b*cos is rounded to float32, then
+    a*cos - b*sin and a*sin + b*cos are rounded to float32 (no fused
+    multiply-add).  x must hold float32-exact values (bf16 inputs do).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    if rotary_dim == 0:
+        return out
+    if rotary_dim % 2 or rotary_dim > x.shape[-1]:
+        raise ValueError("rotary_dim must be even and at most the head dimension")
+    half = rotary_dim // 2
+    x32 = x.astype(np.float32)
+    for n, p in enumerate(positions):
+        c = np.asarray(cos[int(p)], dtype=np.float32)
+        s = np.asarray(sin[int(p)], dtype=np.float32)
+        for i in range(half):
+            ia, ib = (2 * i, 2 * i + 1) if interleaved else (i, i + half)
+            a, b = x32[n, :, ia], x32[n, :, ib]
+            out[n, :, ia] = (a * c[i] - b * s[i]).astype(np.float64)
+            out[n, :, ib] = (a * s[i] + b * c[i]).astype(np.float64)
+    return out
+
+
 def _new_rows(q, k_new, rotary_cos, rotary_sin, positions, rotary_dim, interleaved):
     """The rotated, bf16-rounded query and key of the new tokens."""
     kw = dict(rotary_dim=rotary_dim, interleaved=interleaved)
-    q_rot = round_bf16(rotary_ref(q, rotary_cos, rotary_sin, positions, **kw))
-    k_rot = round_bf16(rotary_ref(k_new, rotary_cos, rotary_sin, positions, **kw))
+    q_rot = round_bf16(rotary_f32(q, rotary_cos, rotary_sin, positions, **kw))
+    k_rot = round_bf16(rotary_f32(k_new, rotary_cos, rotary_sin, positions, **kw))
     return q_rot, k_rot
 
 
@@ -81,7 +112,8 @@ def append_ref(k_new, v_new, k_cache, v_cache, block_table, seqlens_k, *, rotary
     k_new, v_new [B, Hkv, d]; caches [num_pages, page_size, Hkv, d];
     block_table [B, max_pages]; seqlens_k [B] keys cached before the call.
     Request b's new token sits at position p_b = seqlens_k[b]: its key, rotated
-    at p_b and rounded to bf16, and its value go to row p_b % page_size of page
+    at p_b (rotary_f32) and rounded to bf16, and its value go to row
+    p_b % page_size of page
     block_table[b][p_b // page_size].  Requests must not share a target row.
     """
     page = k_cache.shape[1]

@@ -717,6 +717,43 @@ def check_rotary_relative_position():
         assert np.max(np.abs(back - q)) < 1e-12
 
 
+def check_rotary_f32():
+    """The float32 turn rounds each product, then the difference or sum.
+
+    Worked by hand for a = 1 + 2^-7, b = 1, cos = 1 + 2^-23,
+    sin = 1 + 2^-7 + 2^-23 (all float32 values): a*cos = 1 + 2^-7 + 2^-23 +
+    2^-30 rounds to 1 + 2^-7 + 2^-23 and b*sin is exact, so a*cos - b*sin is
+    exactly 0 (float64 gives 2^-30, a fused multiply-add would too);
+    a*sin + b*cos = 2 + 2^-6 + 2^-14 + 2^-22 (float64 adds 2^-30).  On random
+    rows it stays within the rounding bound of the float64 turn:
+    |f32 - f64| <= 2^-23 * (|a cos| + |b sin|) per feature, both layouts."""
+    a, c, s = 1 + 2 ** -7, 1 + 2 ** -23, 1 + 2 ** -7 + 2 ** -23
+    x = np.array([[[a, 1.0]]])
+    r = OK.rotary_f32(x, np.array([[c]]), np.array([[s]]), [0], rotary_dim=2, interleaved=True)
+    assert r[0, 0, 0] == 0.0 and r[0, 0, 1] == 2 + 2 ** -6 + 2 ** -14 + 2 ** -22
+    h = OK.rotary_f32(np.array([[[a, 1.0]]]), np.array([[c]]), np.array([[s]]), [0], rotary_dim=2,
+                      interleaved=False)
+    assert h[0, 0, 0] == 0.0
+    rng = np.random.default_rng(37)
+    x = OK.round_bf16(rng.standard_normal((5, 3, 12)) * 3)
+    ang = rng.uniform(-np.pi, np.pi, size=(40, 4))
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    pos = [0, 7, 39, 3, 7]
+    for inter in (False, True):
+        f32 = OK.rotary_f32(x, cos, sin, pos, rotary_dim=8, interleaved=inter)
+        f64 = OK.rotary_ref(x, cos.astype(np.float64), sin.astype(np.float64), pos, rotary_dim=8,
+                            interleaved=inter)
+        bound = np.zeros_like(x)
+        for n, p in enumerate(pos):
+            for i in range(4):
+                ia, ib = (2 * i, 2 * i + 1) if inter else (i, i + 4)
+                mag = np.abs(x[n, :, ia]) * abs(float(cos[p, i])) + np.abs(x[n, :, ib]) * abs(float(sin[p, i]))
+                mag2 = np.abs(x[n, :, ia]) * abs(float(sin[p, i])) + np.abs(x[n, :, ib]) * abs(float(cos[p, i]))
+                bound[n, :, ia], bound[n, :, ib] = 2 ** -23 * mag, 2 ** -23 * mag2
+        assert np.all(np.abs(f32 - f64) <= bound)
+        assert np.array_equal(f32[..., 8:], x[..., 8:])
+
+
 def _append_case(seed=19):
     rng = np.random.default_rng(seed)
     page, hq, hkv, d, r = 4, 4, 2, 6, 4
@@ -745,7 +782,7 @@ def check_append():
     for inter in (False, True):
         kw = dict(rotary_cos=c["cos"], rotary_sin=c["sin"], rotary_dim=c["r"], interleaved=inter)
         kc, vc = OK.append_ref(c["kn"], c["vn"], c["kc"], c["vc"], c["table"], c["lens"], **kw)
-        k_rot = OK.round_bf16(OK.rotary_ref(c["kn"], c["cos"], c["sin"], c["lens"], rotary_dim=c["r"],
+        k_rot = OK.round_bf16(OK.rotary_f32(c["kn"], c["cos"], c["sin"], c["lens"], rotary_dim=c["r"],
                                             interleaved=inter))
         changed = np.zeros(kc.shape[:3], dtype=bool)
         for b, p in enumerate(c["lens"]):
@@ -771,7 +808,7 @@ def check_decode_append():
         kw = dict(rotary_cos=c["cos"], rotary_sin=c["sin"], rotary_dim=c["r"], interleaved=inter)
         out, lse, q_rot = OK.decode_append_ref(c["q"], c["kn"], c["vn"], c["kc"], c["vc"], c["table"],
                                                c["lens"], softmax_scale=0.45, **kw)
-        rot = lambda x: OK.round_bf16(OK.rotary_ref(x, c["cos"], c["sin"], c["lens"], rotary_dim=c["r"],
+        rot = lambda x: OK.round_bf16(OK.rotary_f32(x, c["cos"], c["sin"], c["lens"], rotary_dim=c["r"],
                                                     interleaved=inter))
         assert np.array_equal(q_rot, rot(c["q"]))
         k_rot = rot(c["kn"])
@@ -802,6 +839,6 @@ ALL_CHECKS = [
     check_numpy_tiled_exactness, check_varlen_packing, check_rows_api,
     check_bwd_sdpa_fp64, check_bwd_finite_differences, check_bwd_identities,
     check_bwd_gqa_and_packing, check_window_forms, check_window_brute_force, check_paged_prefill,
-    check_round_bf16, check_rotary_quarter_turns, check_rotary_relative_position, check_append,
-    check_decode_append,
+    check_round_bf16, check_rotary_quarter_turns, check_rotary_relative_position, check_rotary_f32,
+    check_append, check_decode_append,
 ]

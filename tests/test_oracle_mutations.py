@@ -232,6 +232,27 @@ def _value_not_appended(k_new, v_new, k_cache, v_cache, block_table, seqlens_k, 
 
 
 _orig_append = OK.append_ref
+_orig_f32 = OK.rotary_f32
+
+
+def _f32_fused(x, cos, sin, positions, *, rotary_dim, interleaved):
+    """One rounding per output (as a fused multiply-add chain would give)."""
+    r = OK.rotary_ref(x, cos, sin, positions, rotary_dim=rotary_dim, interleaved=interleaved)
+    return r.astype(np.float32).astype(np.float64)
+
+
+def _f32_sign_flipped(x, cos, sin, positions, *, rotary_dim, interleaved):
+    return _orig_f32(x, cos, None if sin is None else -np.asarray(sin), positions, rotary_dim=rotary_dim,
+                     interleaved=interleaved)
+
+
+def _f32_pairs_swapped(x, cos, sin, positions, *, rotary_dim, interleaved):
+    return _orig_f32(x, cos, sin, positions, rotary_dim=rotary_dim, interleaved=not interleaved)
+
+
+def _f32_position_plus_one(x, cos, sin, positions, *, rotary_dim, interleaved):
+    return _orig_f32(x, cos, sin, [int(p) + 1 for p in positions], rotary_dim=rotary_dim,
+                     interleaved=interleaved)
 
 KV_MUTANTS = {
     "rotary_sign_flipped": ("rotary_ref", _rotary_sign_flipped),
@@ -242,6 +263,10 @@ KV_MUTANTS = {
     "query_not_rotated": ("_new_rows", _query_not_rotated),
     "append_previous_row": ("append_ref", _append_previous_row),
     "value_not_appended": ("append_ref", _value_not_appended),
+    "rotary_f32_fused": ("rotary_f32", _f32_fused),
+    "rotary_f32_sign_flipped": ("rotary_f32", _f32_sign_flipped),
+    "rotary_f32_pairs_swapped": ("rotary_f32", _f32_pairs_swapped),
+    "rotary_f32_position_plus_one": ("rotary_f32", _f32_position_plus_one),
 }
 
 
