@@ -51,6 +51,8 @@ _SIGNATURES = {
     "attn_bwd_workspace_bytes": ([_I, _I], ctypes.c_size_t),
     "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "attn_decode_combine": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "attn_decode_kvcache": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                             _I, _I, _I, _F, _P, _P, _P, _P, _P, _P], _I),
     "attn_decode_num_splits": ([_I, _I], _I),
     "attn_decode_default_chunk": ([_I, _I, _I, _I], _I),
     "attn_decode_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
@@ -379,6 +381,82 @@ def attn_decode(q, k_cache, v_cache, block_table, seqlens_k, *, max_seqlen_k, so
                                  chunk_tokens=chunk_tokens, num_splits=n,
                                  softmax_scale=softmax_scale, stream=stream)
     return attn_decode_combine(po, pl, seqlens_k, chunk_tokens=chunk_tokens, stream=stream)
+
+
+def attn_decode_kvcache(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, *, max_seqlen_k,
+                        softmax_scale, rotary_cos=None, rotary_sin=None, rotary_interleaved=False,
+                        chunk_tokens=None, q_rot=None, out_partial=None, lse_partial=None, out=None,
+                        lse=None, return_lse=True, stream=None):
+    """Append one token per request to the paged cache (in place), then decode.
+
+    q [B, Hq, d]; k_new, v_new [B, Hkv, d] bf16; caches [P, 256, Hkv, d] bf16
+    (updated); block_table int32 [B, maxp]; seqlens_k int32 [B], keys cached
+    before the call (the new token goes to position seqlens_k[b]; seqlens_k is
+    not changed).  max_seqlen_k bounds seqlens_k (before the append) and sizes
+    the splits.  rotary_cos/rotary_sin float32 [max_pos, rotary_dim / 2] turn q
+    and the new key at their position (None: no rotary).  Returns (out, lse,
+    q_rot); q_rot is None without rotary.
+    """
+    dev = q.device
+    for t, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expects q [B,Hq,d] and caches [P,page,Hkv,d]")
+    batch, hq, d = q.shape
+    num_pages, page, hkv, dk = k_cache.shape
+    if (dk != d or tuple(k_new.shape) != (batch, hkv, d) or v_new.shape != k_new.shape
+            or block_table.dim() != 2 or block_table.shape[0] != batch or seqlens_k.shape != (batch,)):
+        raise ValueError("inconsistent decode shapes")
+    rot = 0
+    max_pos = 0
+    if (rotary_cos is None) != (rotary_sin is None):
+        raise ValueError("give both rotary_cos and rotary_sin, or neither")
+    if rotary_cos is not None:
+        _need(rotary_cos, "rotary_cos", torch.float32, dev)
+        _need(rotary_sin, "rotary_sin", torch.float32, dev)
+        if rotary_cos.dim() != 2 or rotary_sin.shape != rotary_cos.shape:
+            raise ValueError("rotary tables must both be [max_pos, rotary_dim / 2]")
+        max_pos, rot = rotary_cos.shape[0], 2 * rotary_cos.shape[1]
+        if q_rot is None:
+            q_rot = torch.empty_like(q)
+        _need(q_rot, "q_rot", torch.bfloat16, dev)
+        if q_rot.shape != q.shape:
+            raise ValueError("q_rot must have q's shape")
+    else:
+        q_rot = None
+    total = int(max_seqlen_k) + 1
+    if chunk_tokens is None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        chunk_tokens = attn_decode_default_chunk(batch, hkv, total, cus)
+    n = max(1, attn_decode_num_splits(total, chunk_tokens))
+    if out_partial is None:
+        out_partial = torch.empty((n, batch, hq, d), dtype=torch.float32, device=dev)
+    if lse_partial is None:
+        lse_partial = torch.empty((n, batch, hq), dtype=torch.float32, device=dev)
+    _need(out_partial, "out_partial", torch.float32, dev)
+    _need(lse_partial, "lse_partial", torch.float32, dev)
+    if out_partial.numel() < n * batch * hq * d or lse_partial.numel() < n * batch * hq:
+        raise ValueError("partial buffers are too small")
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_kvcache(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seqlens_k), _ptr(rotary_cos), _ptr(rotary_sin), rot, int(bool(rotary_interleaved)),
+            max_pos, batch, hq, hkv, d, page, block_table.shape[1], num_pages, int(chunk_tokens), n,
+            float(softmax_scale), _ptr(q_rot), _ptr(out_partial), _ptr(lse_partial), _ptr(out),
+            _ptr(lse), _stream(stream, dev))
+    _check(st)
+    return out, lse, q_rot
 
 
 def attn_check_cu_seqlens(cu_seqlens, total, max_seqlen):

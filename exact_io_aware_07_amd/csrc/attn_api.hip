@@ -321,6 +321,127 @@ attn_status_t attn_decode_combine(const float* out_partial, const float* lse_par
                       "attn_decode_combine launch");
 }
 
+attn_status_t attn_decode_kvcache(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                  void* v_cache, const int32_t* block_table, const int32_t* seqlens_k,
+                                  const float* rotary_cos, const float* rotary_sin, int rotary_dim,
+                                  int rotary_interleaved, int rotary_max_pos, int batch,
+                                  int num_heads_q, int num_heads_kv, int head_dim, int page_size,
+                                  int max_pages_per_seq, int num_pages, int chunk_tokens,
+                                  int num_splits, float softmax_scale, void* q_rot,
+                                  float* out_partial, float* lse_partial, void* out, float* lse,
+                                  void* stream) {
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !block_table || !seqlens_k || !out_partial ||
+        !lse_partial || !out)
+        return fail(ATTN_ERR_NULL, "q, k_new, v_new, the caches, block_table, seqlens_k, the partials "
+                    "and out must be non-NULL");
+    if (rotary_dim != 0 && (!rotary_cos || !rotary_sin || !q_rot))
+        return fail(ATTN_ERR_NULL, "rotary_dim > 0 needs rotary_cos, rotary_sin and q_rot");
+    if (batch < 1 || num_heads_q < 1 || num_heads_kv < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
+        num_splits < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d num_heads_q=%d num_heads_kv=%d "
+                    "max_pages_per_seq=%d num_pages=%d num_splits=%d", batch, num_heads_q,
+                    num_heads_kv, max_pages_per_seq, num_pages, num_splits);
+    if (num_heads_q % num_heads_kv)
+        return fail(ATTN_ERR_SHAPE, "num_heads_kv=%d does not divide num_heads_q=%d", num_heads_kv,
+                    num_heads_q);
+    if (num_heads_q / num_heads_kv > 64)
+        return fail(ATTN_ERR_UNSUPPORTED, "more than 64 query heads per K/V head");
+    if (!head_dim_supported(head_dim))
+        return fail(ATTN_ERR_UNSUPPORTED, "head_dim=%d not in {64,128,256}", head_dim);
+    if (page_size != 256) return fail(ATTN_ERR_UNSUPPORTED, "page_size must be 256 (got %d)", page_size);
+    if (chunk_tokens < page_size || chunk_tokens % page_size)
+        return fail(ATTN_ERR_UNSUPPORTED, "chunk_tokens=%d is not a positive multiple of page_size",
+                    chunk_tokens);
+    if (rotary_dim < 0 || rotary_dim % 2 || rotary_dim > head_dim)
+        return fail(ATTN_ERR_SHAPE, "rotary_dim=%d must be even and in [0, head_dim=%d]", rotary_dim,
+                    head_dim);
+    if (rotary_dim > 0 && rotary_max_pos < 1)
+        return fail(ATTN_ERR_SHAPE, "rotary_max_pos=%d must be >= 1", rotary_max_pos);
+    if (rotary_interleaved != 0 && rotary_interleaved != 1)
+        return fail(ATTN_ERR_SHAPE, "rotary_interleaved must be 0 or 1");
+    attn_status_t st = check_scale(softmax_scale);
+    if (st != ATTN_OK) return st;
+
+    // Every written region must be disjoint from every other region.
+    const size_t qb = (size_t)batch * num_heads_q * head_dim * 2;
+    const size_t kb = (size_t)batch * num_heads_kv * head_dim * 2;
+    const size_t cb = (size_t)num_pages * page_size * num_heads_kv * head_dim * 2;
+    const size_t tb = (size_t)rotary_max_pos * (size_t)(rotary_dim / 2) * 4;
+    struct Region { const void* p; size_t n; bool written; };
+    const Region reg[] = {
+        {q, qb, false}, {k_new, kb, false}, {v_new, kb, false},
+        {block_table, (size_t)batch * max_pages_per_seq * 4, false}, {seqlens_k, (size_t)batch * 4, false},
+        {rotary_dim ? rotary_cos : nullptr, tb, false}, {rotary_dim ? rotary_sin : nullptr, tb, false},
+        {k_cache, cb, true}, {v_cache, cb, true}, {rotary_dim ? q_rot : nullptr, qb, true},
+        {out_partial, (size_t)num_splits * batch * num_heads_q * head_dim * 4, true},
+        {lse_partial, (size_t)num_splits * batch * num_heads_q * 4, true},
+        {out, qb, true}, {lse, (size_t)batch * num_heads_q * 4, true},
+    };
+    const int nreg = (int)(sizeof(reg) / sizeof(reg[0]));
+    for (int i = 0; i < nreg; ++i)
+        for (int j = i + 1; j < nreg; ++j)
+            if ((reg[i].written || reg[j].written) && overlap(reg[i].p, reg[i].n, reg[j].p, reg[j].n))
+                return fail(ATTN_ERR_ALIAS, "argument regions %d and %d overlap (a written region must "
+                            "not overlap any other argument)", i, j);
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    attn::AppendParams a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.k_cache = static_cast<uint16_t*>(k_cache);
+    a.v_cache = static_cast<uint16_t*>(v_cache);
+    a.block_table = block_table;
+    a.seqlens = seqlens_k;
+    a.rot_cos = rotary_cos;
+    a.rot_sin = rotary_sin;
+    a.q_rot = static_cast<uint16_t*>(q_rot);
+    a.batch = batch;
+    a.hq = num_heads_q;
+    a.hkv = num_heads_kv;
+    a.max_pages = max_pages_per_seq;
+    a.num_pages = num_pages;
+    a.rot_dim = rotary_dim;
+    a.interleaved = rotary_interleaved;
+    a.max_pos = rotary_max_pos;
+    st = hip_status(attn::launch_decode_append(a, head_dim, s), "attn_decode_kvcache append launch");
+    if (st != ATTN_OK) return st;
+
+    attn::DecodeParams p{};
+    p.q = rotary_dim ? static_cast<const uint16_t*>(q_rot) : static_cast<const uint16_t*>(q);
+    p.k_cache = static_cast<const uint16_t*>(k_cache);
+    p.v_cache = static_cast<const uint16_t*>(v_cache);
+    p.block_table = block_table;
+    p.seqlens = seqlens_k;
+    p.out_part = out_partial;
+    p.lse_part = lse_partial;
+    p.batch = batch;
+    p.hq = num_heads_q;
+    p.hkv = num_heads_kv;
+    p.max_pages = max_pages_per_seq;
+    p.num_pages = num_pages;
+    p.chunk = chunk_tokens;
+    p.n_splits = num_splits;
+    p.scale = softmax_scale;
+    p.len_add = 1;
+    p.len_limit = rotary_dim ? rotary_max_pos : 0;
+    st = hip_status(attn::launch_decode_split(p, head_dim, s), "attn_decode_kvcache split launch");
+    if (st != ATTN_OK) return st;
+
+    attn::CombineParams c{};
+    c.out_part = out_partial;
+    c.lse_part = lse_partial;
+    c.seqlens = seqlens_k;
+    c.out = static_cast<uint16_t*>(out);
+    c.lse = lse;
+    c.batch = batch;
+    c.hq = num_heads_q;
+    c.chunk = chunk_tokens;
+    c.n_splits = num_splits;
+    c.len_add = 1;
+    return hip_status(attn::launch_decode_combine(c, head_dim, s), "attn_decode_kvcache combine launch");
+}
+
 int attn_decode_num_splits(int max_seqlen_k, int chunk_tokens) {
     if (max_seqlen_k <= 0 || chunk_tokens <= 0) return 0;
     return (int)(((long)max_seqlen_k + chunk_tokens - 1) / chunk_tokens);

@@ -74,17 +74,17 @@ void attn_decode_split_kernel(DecodeParams p) {
     const int g = p.hq / p.hkv;
     const int hq0 = kvh * g;
 
-    int Nk = p.seqlens[b];
-    bool bad = false;
-    if (Nk < 0) {
-        Nk = 0;
+    const int raw_len = p.seqlens[b];
+    bool bad = raw_len < 0;
+    long nk_l = bad ? 0 : (long)raw_len + p.len_add;
+    long cap = (long)p.max_pages * kPage;
+    if (p.len_limit > 0 && p.len_limit < cap) cap = p.len_limit;
+    if (cap > 0x7fffffffL - kPage) cap = 0x7fffffffL - kPage;  // key offsets stay in int range
+    if (nk_l > cap) {
+        nk_l = cap;
         bad = true;
     }
-    const long cap = (long)p.max_pages * kPage;
-    if (Nk > cap) {
-        Nk = (int)cap;
-        bad = true;
-    }
+    int Nk = (int)nk_l;
     const int key_begin = split * p.chunk;
     if (key_begin >= Nk && !(bad && split == 0)) return;
     const int key_end = min(Nk, key_begin + p.chunk);
@@ -301,11 +301,12 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(CombineParams p
     const int bh = blockIdx.x;
     const int b = bh / p.hq;
     const int lane = threadIdx.x;
-    const int Nk = p.seqlens[b];
-    const int n = Nk > 0 ? (Nk + p.chunk - 1) / p.chunk : 0;
+    const int raw_len = p.seqlens[b];
+    const long Nk = raw_len < 0 ? -1 : (long)raw_len + p.len_add;
+    const long n = Nk > 0 ? (Nk + p.chunk - 1) / p.chunk : 0;
     const bool bad = Nk < 0 || n > p.n_splits;
     const long split_stride = (long)p.batch * p.hq;
-    const int nn = bad ? 0 : n;
+    const int nn = bad ? 0 : (int)n;
     const float* rows = p.out_part + (long)bh * D + lane;
     float acc[PER];
 #pragma unroll
@@ -366,6 +367,95 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(CombineParams p
     }
     if (p.lse != nullptr && lane == 0)
         p.lse[bh] = poison ? NAN : (L > 0.0f ? M + __logf(L) : -INFINITY);
+}
+
+// The value of feature e of a bf16 row after the rotary turn of its pair
+// (features i and i + rot / 2, or 2i and 2i + 1 when interleaved): the pair
+// (a, b) turns into (a cos - b sin, a sin + b cos) with the cosine and sine of
+// pair index i at this position; features from rot on are unchanged.
+__device__ __forceinline__ float bf16_at(const uint16_t* x, int e) {
+    return __builtin_bit_cast(float, (uint32_t)x[e] << 16);
+}
+
+// Each product is rounded to float32 and then the difference or sum: the
+// contraction into fused multiply-adds is switched off, so the rounding to
+// bf16 that follows sees a fixed, reproducible float32 value.
+__device__ __forceinline__ float rotary_feature(const uint16_t* x, int e, const float* cs, const float* sn,
+                                                int rot, bool inter) {
+#pragma clang fp contract(off)
+    const float v = bf16_at(x, e);
+    if (e >= rot) return v;
+    const int half = rot >> 1;
+    const bool first = inter ? (e & 1) == 0 : e < half;
+    const int i = inter ? (e >> 1) : (first ? e : e - half);
+    const int partner = inter ? (first ? e + 1 : e - 1) : (first ? e + half : e - half);
+    const float w = bf16_at(x, partner);
+    const float c = cs[i], s = sn[i];
+    return first ? v * c - w * s : w * s + v * c;
+}
+
+// Append kernel: one wave per (request, row).  Rows 0 .. hkv-1 write K/V head
+// `row` of the new token into the cache at position seqlens[b] (the key after
+// its rotary turn, rounded to bf16; the value as given); rows hkv .. hkv+hq-1
+// write query head `row - hkv` after its turn into q_rot.  A request whose
+// position is negative, has no room in its table (or rotary table), or falls
+// on an out-of-range page id writes nothing into the cache and NaN into its
+// q_rot rows; the split kernel flags the same request and its output is NaN.
+template <int D>
+__global__ __launch_bounds__(64) void attn_decode_append_kernel(AppendParams p) {
+    const bool rope = p.rot_dim > 0;
+    const int rows = p.hkv + (rope ? p.hq : 0);
+    const int b = blockIdx.x / rows;
+    const int r = blockIdx.x % rows;
+    const int lane = threadIdx.x;
+    const int pos = p.seqlens[b];
+    bool bad = pos < 0 || (long)pos >= (long)p.max_pages * kPage || (rope && pos >= p.max_pos);
+    int phys = 0;
+    if (!bad) {
+        phys = p.block_table[(long)b * p.max_pages + pos / kPage];
+        bad = phys < 0 || phys >= p.num_pages;
+    }
+    const float* cs = rope && !bad ? p.rot_cos + (long)pos * (p.rot_dim >> 1) : nullptr;
+    const float* sn = rope && !bad ? p.rot_sin + (long)pos * (p.rot_dim >> 1) : nullptr;
+    const bool inter = p.interleaved != 0;
+    if (r < p.hkv) {
+        if (bad) return;
+        const long src = ((long)b * p.hkv + r) * D;
+        const long dst = (((long)phys * kPage + pos % kPage) * p.hkv + r) * D;
+#pragma unroll
+        for (int e = lane; e < D; e += 64) {
+            const float kv = rope ? rotary_feature(p.k_new + src, e, cs, sn, p.rot_dim, inter)
+                                  : bf16_at(p.k_new + src, e);
+            p.k_cache[dst + e] = (uint16_t)(pack_bf16x2(kv, 0.0f) & 0xffffu);
+            p.v_cache[dst + e] = p.v_new[src + e];
+        }
+    } else {
+        const long row = ((long)b * p.hq + (r - p.hkv)) * D;
+#pragma unroll
+        for (int e = lane; e < D; e += 64) {
+            const float qv = bad ? NAN : rotary_feature(p.q + row, e, cs, sn, p.rot_dim, inter);
+            p.q_rot[row + e] = (uint16_t)(pack_bf16x2(qv, 0.0f) & 0xffffu);
+        }
+    }
+}
+
+hipError_t launch_decode_append(const AppendParams& p, int head_dim, hipStream_t s) {
+    const long grid = (long)p.batch * (p.hkv + (p.rot_dim > 0 ? p.hq : 0));
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    switch (head_dim) {
+        case 64:
+            hipLaunchKernelGGL(attn_decode_append_kernel<64>, dim3((unsigned)grid), dim3(64), 0, s, p);
+            break;
+        case 128:
+            hipLaunchKernelGGL(attn_decode_append_kernel<128>, dim3((unsigned)grid), dim3(64), 0, s, p);
+            break;
+        case 256:
+            hipLaunchKernelGGL(attn_decode_append_kernel<256>, dim3((unsigned)grid), dim3(64), 0, s, p);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <int D, int QB, int HPW>

@@ -34,6 +34,24 @@ struct DecodeParams {
     float* lse_part;
     int batch, hq, hkv, max_pages, num_pages, chunk, n_splits;
     float scale;
+    int len_add = 0;    // keys appended just before this launch: request b attends over seqlens[b] + len_add
+    int len_limit = 0;  // > 0: a request attending over more keys than this is invalid (NaN)
+};
+
+// In-place append of one new token per request, with optional rotary turns.
+struct AppendParams {
+    const uint16_t* q;      // [batch, hq, d]
+    const uint16_t* k_new;  // [batch, hkv, d]
+    const uint16_t* v_new;
+    uint16_t* k_cache;      // [num_pages, 256, hkv, d]
+    uint16_t* v_cache;
+    const int32_t* block_table;
+    const int32_t* seqlens;  // position of the new token = keys cached before the call
+    const float* rot_cos;    // [max_pos, rot_dim / 2]; unused when rot_dim == 0
+    const float* rot_sin;
+    uint16_t* q_rot;         // [batch, hq, d]; written when rot_dim > 0
+    int batch, hq, hkv, max_pages, num_pages;
+    int rot_dim, interleaved, max_pos;
 };
 
 struct CombineParams {
@@ -43,6 +61,7 @@ struct CombineParams {
     uint16_t* out;
     float* lse;  // may be null
     int batch, hq, chunk, n_splits;
+    int len_add = 0;  // as in DecodeParams
 };
 
 struct BwdParams {
@@ -68,5 +87,6 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_decode_combine(const CombineParams& p, int head_dim, hipStream_t s);
+hipError_t launch_decode_append(const AppendParams& p, int head_dim, hipStream_t s);
 
 }  // namespace attn

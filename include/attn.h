@@ -233,6 +233,63 @@ attn_status_t attn_decode_combine(const float* out_partial, const float* lse_par
                                   int head_dim, int chunk_tokens, int num_splits,
                                   void* out, float* lse, void* stream);
 
+/*
+ * attn_decode_kvcache -- one decode step that first appends the new token to
+ * the paged cache in place, with optional rotary embedding, then decodes over
+ * the cache including it ("Deep Dive - FlashAttention", "Paged KV is a
+ * lookup, not a cache manager": the cached-decode call can update the cache
+ * in place and apply rotary embeddings, into space the caller reserved;
+ * "FlashAttention: Part 1", sections 4.1 and 4.2: rotary embedding turns Q
+ * and K by position before attention).
+ *
+ *   q            [batch, num_heads_q, head_dim] bf16, the new token's queries
+ *   k_new, v_new [batch, num_heads_kv, head_dim] bf16, its key and value
+ *   k_cache,
+ *   v_cache      [num_pages, page_size, num_heads_kv, head_dim] bf16, updated
+ *                in place
+ *   block_table, as in attn_decode_splitkv
+ *   seqlens_k    [batch] int32: keys cached BEFORE this call.  The new token
+ *                takes position p = seqlens_k[b]: its key and value are
+ *                written to row p % page_size of page block_table[b][p /
+ *                page_size], and request b then attends over p + 1 keys.
+ *                seqlens_k is not modified; the caller advances it.
+ *   rotary_dim   0 (no rotary: the key is stored and the query used as given)
+ *                or an even number <= head_dim of leading features to turn.
+ *                Feature pairs are (i, i + rotary_dim/2) when
+ *                rotary_interleaved == 0, (2i, 2i+1) when 1; pair i at
+ *                position p turns (a, b) into (a cos - b sin, a sin + b cos)
+ *                with cos = rotary_cos[p * rotary_dim/2 + i] and likewise sin
+ *                (float32 tables [rotary_max_pos, rotary_dim/2], the caller's
+ *                frequencies).  Both q and the new key turn at position p, in
+ *                float32, and are rounded to bf16 (nearest even).
+ *   q_rot        [batch, num_heads_q, head_dim] bf16, written with the turned
+ *                queries when rotary_dim > 0 (may be NULL when 0)
+ *   chunk_tokens, num_splits, out_partial, lse_partial: as in
+ *                attn_decode_splitkv, for lengths seqlens_k[b] + 1
+ *                (num_splits >= ceil((max_b seqlens_k[b] + 1) / chunk_tokens))
+ *   out, lse     as in attn_decode_combine (lse may be NULL)
+ * A request whose position is negative, has no room (p >= max_pages_per_seq *
+ * page_size, or p >= rotary_max_pos with rotary), or falls on a page id
+ * outside [0, num_pages) writes nothing into the caches, gets NaN q_rot rows
+ * and NaN out/lse; it never faults.  Requests must not share the cache row
+ * they append to, and no request may read a row another request of the same
+ * call appends (the writes would race).  Every written region (caches,
+ * q_rot, partials, out, lse) must be disjoint from every other argument
+ * (ATTN_ERR_ALIAS).  Requirements otherwise as attn_decode_splitkv.
+ * Enqueues three kernels (append, split, combine) on the stream; argument
+ * errors are returned before any of them, a launch failure after the first
+ * can leave the earlier ones enqueued.
+ */
+attn_status_t attn_decode_kvcache(const void* q, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, const int32_t* block_table,
+                                  const int32_t* seqlens_k, const float* rotary_cos,
+                                  const float* rotary_sin, int rotary_dim, int rotary_interleaved,
+                                  int rotary_max_pos, int batch, int num_heads_q, int num_heads_kv,
+                                  int head_dim, int page_size, int max_pages_per_seq, int num_pages,
+                                  int chunk_tokens, int num_splits, float softmax_scale,
+                                  void* q_rot, float* out_partial, float* lse_partial, void* out,
+                                  float* lse, void* stream);
+
 /* ceil(max_seqlen_k / chunk_tokens), the smallest valid num_splits (0 if
  * max_seqlen_k <= 0 or chunk_tokens <= 0). */
 int attn_decode_num_splits(int max_seqlen_k, int chunk_tokens);

@@ -126,6 +126,41 @@ def test_fwd_ex_rejects(kw, code):
     assert fwd_ex(**kw) == code
 
 
+def _at(i):
+    return ctypes.c_void_p(0x1000000 * (i + 1))   # 16 MiB apart: no two regions overlap
+
+
+def kvc(**kw):
+    """attn_decode_kvcache with B=2, Hq=8, Hkv=2, d=128, 4 pages, 2 splits; every case fails validation."""
+    a = dict(q=_at(0), kn=_at(1), vn=_at(2), kc=_at(3), vc=_at(4), bt=_at(5), sl=_at(6), cos=NULL, sin=NULL,
+             rot=0, inter=0, maxpos=0, batch=2, hq=8, hkv=2, d=128, page=256, maxp=2, npages=4, chunk=256,
+             nsplit=2, scale=0.125, qrot=NULL, po=_at(7), pl=_at(8), out=_at(9), lse=_at(10))
+    a.update(kw)
+    return ea.lib().attn_decode_kvcache(
+        a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["sl"], a["cos"], a["sin"], a["rot"], a["inter"],
+        a["maxpos"], a["batch"], a["hq"], a["hkv"], a["d"], a["page"], a["maxp"], a["npages"], a["chunk"],
+        a["nsplit"], a["scale"], a["qrot"], a["po"], a["pl"], a["out"], a["lse"], None)
+
+
+ROPE = dict(rot=64, cos=_at(11), sin=_at(12), qrot=_at(13), maxpos=100)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(kn=NULL), 1), (dict(vn=NULL), 1), (dict(kc=NULL), 1), (dict(vc=NULL), 1),
+    (dict(bt=NULL), 1), (dict(sl=NULL), 1), (dict(po=NULL), 1), (dict(pl=NULL), 1), (dict(out=NULL), 1),
+    (dict(ROPE, cos=NULL), 1), (dict(ROPE, sin=NULL), 1), (dict(ROPE, qrot=NULL), 1),
+    (dict(batch=0), 2), (dict(hq=6, hkv=4), 2), (dict(nsplit=0), 2), (dict(ROPE, rot=3), 2),
+    (dict(ROPE, rot=256), 2), (dict(ROPE, rot=-2), 2), (dict(ROPE, maxpos=0), 2), (dict(inter=2), 2),
+    (dict(d=96), 3), (dict(page=128), 3), (dict(chunk=100), 3), (dict(hq=130, hkv=2), 3),
+    (dict(scale=0.0), 4), (dict(ROPE, scale=float("nan")), 4),
+    (dict(kc=_at(0)), 5), (dict(vc=ctypes.c_void_p(0x4000000 + 64)), 5), (dict(out=_at(0)), 5),
+    (dict(lse=_at(9)), 5), (dict(ROPE, qrot=_at(11)), 5), (dict(ROPE, out=_at(13)), 5),
+    (dict(po=_at(1)), 5), (dict(pl=_at(5)), 5), (dict(ROPE, kc=_at(12)), 5),
+])
+def test_decode_kvcache_rejects(kw, code):
+    assert kvc(**kw) == code
+
+
 DQ = ctypes.c_void_p(0x60000000)
 DK = ctypes.c_void_p(0x70000000)
 DV = ctypes.c_void_p(0x78000000)

@@ -6,5 +6,7 @@ from .gen import (  # noqa: F401
     varlen_case,
     decode_lengths,
     decode_case,
+    append_case,
+    rotary_tables,
     config_case,
 )

@@ -137,6 +137,37 @@ def decode_case(seqlens, Hq, Hkv, d, seed, *, page=PAGE_SIZE, device="cpu", pois
                 B=B, Hq=Hq, Hkv=Hkv, d=d, page=page, num_pages=n_pool)
 
 
+def rotary_tables(max_pos, rotary_dim, base=10000.0, device="cpu"):
+    """float32 cos/sin tables [max_pos, rotary_dim / 2] of RoFormer's angles.
+
+    Pair i at position p turns by p * base ** (-2 i / rotary_dim); the angles
+    and their cosines and sines are formed in float64 and rounded once.  These
+    are inputs (a model's choice of frequencies), not part of the method.
+    """
+    i = torch.arange(rotary_dim // 2, dtype=torch.float64)
+    theta = base ** (-2.0 * i / rotary_dim)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * theta[None, :]
+    return (torch.cos(ang).to(torch.float32).to(device), torch.sin(ang).to(torch.float32).to(device))
+
+
+def append_case(seqlens, Hq, Hkv, d, seed, *, device="cpu", poison=False, extra_table_cols=0):
+    """Inputs of one decode step that appends a token to each request.
+
+    The paged cache is decode_case's for lengths seqlens[b] + 1, so each
+    request's table already names the page of its new position; seqlens_k is
+    set to seqlens (the keys cached before the step), and the row at position
+    seqlens[b] holds random data that the append overwrites.  k_new, v_new
+    [B, Hkv, d] are bf16 N(0, 1) from their own seeded generator.
+    """
+    case = decode_case([int(n) + 1 for n in seqlens], Hq, Hkv, d, seed, device=device, poison=poison,
+                       extra_table_cols=extra_table_cols)
+    case["seqlens_k"] = torch.tensor([int(n) for n in seqlens], dtype=torch.int32)
+    g = _gen(seed + 500, device)
+    case["k_new"] = _randn_bf16((len(seqlens), Hkv, d), g, device)
+    case["v_new"] = _randn_bf16((len(seqlens), Hkv, d), g, device)
+    return case
+
+
 def config_case(name, *, device="cpu", d=None, poison=False):
     """Materialise one of CONFIGS (d overrides the head dim of the varlen case)."""
     c = CONFIGS[name]
