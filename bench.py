@@ -186,6 +186,58 @@ def time_backward(ea, pc, out, lse, stream, torch, reps=10):
             "workload": PREFILL}
 
 
+def kvcache_bytes(case, rotary_dim):
+    """Algorithmic bytes of a decode step that appends one token per request:
+    the cached K/V rows read, the new key and value read once and written once
+    into the cache, q read, out and lse written, the used table entries,
+    lengths and cos/sin rows.  The turned-query round trip is overhead."""
+    lens = case["seqlens_k"].tolist()
+    B, Hq, Hkv, d, page = case["B"], case["Hq"], case["Hkv"], case["d"], case["page"]
+    kv = sum(lens) * Hkv * d * 2 * 2
+    new = 2 * (2 * B * Hkv * d * 2)
+    qo = 2 * B * Hq * d * 2 + 4 * B * Hq
+    table = 4 * sum(-(-(n + 1) // page) for n in lens) + 4 * B
+    rot = B * (rotary_dim // 2) * 4 * 2
+    return kv + new + qo + table + rot
+
+
+def time_decode_kvcache(ea, W, dev, props, stream, torch, reps=20):
+    """attn_decode_kvcache (append + rotary, split, combine in one call) on the
+    paged decode workload's lengths with one appended token per request and a
+    rotary turn over all 128 features; timed apart from the step."""
+    c = W.CONFIGS[DECODE]
+    lens = W.decode_lengths(c["B"], c["nk_lo"], c["nk_hi"], c["seed"])
+    kc = W.append_case(lens, c["Hq"], c["Hkv"], c["d"], seed=c["seed"], device=dev)
+    table, seq = kc["block_table"].to(dev), kc["seqlens_k"].to(dev)
+    cos, sin = (t.to(dev) for t in W.rotary_tables(max(lens) + 1, c["d"]))
+    total = max(lens) + 1
+    chunk = ea.attn_decode_default_chunk(c["B"], c["Hkv"], total, props.multi_processor_count)
+    n = ea.attn_decode_num_splits(total, chunk)
+    bufs = dict(q_rot=torch.empty_like(kc["q"]),
+                out_partial=torch.empty((n, c["B"], c["Hq"], c["d"]), dtype=torch.float32, device=dev),
+                lse_partial=torch.empty((n, c["B"], c["Hq"]), dtype=torch.float32, device=dev),
+                out=torch.empty_like(kc["q"]), lse=torch.empty((c["B"], c["Hq"]), dtype=torch.float32, device=dev))
+
+    def run():
+        ea.attn_decode_kvcache(kc["q"], kc["k_new"], kc["v_new"], kc["k_cache"], kc["v_cache"], table, seq,
+                               max_seqlen_k=max(lens), softmax_scale=c["d"] ** -0.5, rotary_cos=cos,
+                               rotary_sin=sin, chunk_tokens=chunk, stream=stream, **bufs)
+
+    for _ in range(3):
+        run()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    nbytes = kvcache_bytes(kc, c["d"])
+    return {"call_ms_mean": round(ms, 4), "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "algorithmic_bytes": nbytes, "chunk_tokens": chunk, "splits": n,
+            "workload": DECODE + " with one appended token per request, rotary over all 128 features"}
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
     import numpy as np
@@ -243,6 +295,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the separately timed attn_bwd leg (not part of the step)")
+    ap.add_argument("--no-kvcache", action="store_true",
+                    help="skip the separately timed attn_decode_kvcache leg (not part of the step)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for counter scaling)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -331,6 +385,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     bwd = None if args.no_backward else time_backward(ea, pc, out, lse, stream, torch)
+    kvc = None if args.no_kvcache else time_decode_kvcache(ea, W, dev, props, stream, torch)
     pre = [e[0].elapsed_time(e[1]) for e in events]
     spl = [e[1].elapsed_time(e[2]) for e in events]
     cmb = [e[2].elapsed_time(e[3]) for e in events]
@@ -387,6 +442,8 @@ def main():
     }
     if bwd is not None:
         rec["backward"] = bwd
+    if kvc is not None:
+        rec["decode_kvcache"] = kvc
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pc)
     print(json.dumps(rec), flush=True)
