@@ -13,7 +13,10 @@ Sources (page title, section):
     "Paged KV is a lookup, not a cache manager" (also the in-place cache append).
   * "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)":
     "Runnable Example: Measuring the IO Gap", "Decode-Time Kernels".
-  * "Flash Attention: A Complete Architectural Autopsy": "Part 1".
+  * "Flash Attention: A Complete Architectural Autopsy": "Part 1", "FP8 Path and
+    Quantization" (module fp8).
+  * "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)",
+    "FlashAttention-3": block quantisation and incoherent processing (module fp8).
   * "FlashAttention: Part 1": sections 2.2, 3.5, 4.1, 4.2 (rotary embedding as a
     transform of Q and K before attention; module kvcache).
 
@@ -24,7 +27,11 @@ variable-length batches); those two are "parity unpinned".  The rotary
 formula and the bf16 rounding of rotated rows are readings (the pages give
 neither); they are pinned to hand-worked turns, RoFormer's relative-position
 property, a hand-worked float32 rounding case with the float64 error bound,
-and PyTorch's float32 -> bfloat16 conversion.
+and PyTorch's float32 -> bfloat16 conversion.  Module fp8 (E4M3 codec, the
+float32 Walsh-Hadamard turn, block quantisation, the V^T layout, attention on
+dequantised operands and the bound on the error of rounding probabilities to
+E4M3) is pinned to PyTorch's float8_e4m3fn, scipy's Hadamard matrix, hand-worked
+codes and positions, and a slow tile model of the probability rounding.
 """
 from .attention import (  # noqa: F401
     kv_head_for_queries,

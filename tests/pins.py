@@ -12,6 +12,7 @@ import numpy as np
 
 import oracle.attention as OA
 import oracle.kvcache as OK
+import oracle.fp8 as OF
 from brute_force import brute_attention
 from tiled_recurrence import combine_partials, tiled_attention, tiled_row
 
@@ -832,6 +833,155 @@ def check_decode_append():
     assert np.array_equal(q_rot, OK.round_bf16(c["q"]))
 
 
+# ---- FP8 forward -------------------------------------------------------------
+
+
+def check_e4m3_codec():
+    """E4M3 (OCP "fn") against PyTorch's float8_e4m3fn: every code decodes to
+    the same value (NaN codes included), encode inverts decode, and encoding
+    float32 values (ties between neighbours and subnormals included) equals
+    PyTorch's conversion.  Hand cases: 448 -> 0x7E; 464 lies halfway between
+    448 and 480 and goes to the even 448; 465 rounds to 480 > 448 -> NaN;
+    2^-9 is the smallest subnormal 0x01; 2^-10 is halfway to it and goes to 0;
+    3 * 2^-10 is halfway between codes 1 and 2 and goes to 2; 1 + 2^-4 is
+    halfway between 1 (0x38) and 1.125 and goes to 0x38."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    dec = OF.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(dec), np.isnan(ref)) and np.array_equal(dec[~np.isnan(dec)], ref[~np.isnan(ref)])
+    fin = ~np.isnan(dec)
+    assert np.array_equal(OF.e4m3_encode(dec[fin]), codes[fin])
+    rng = np.random.default_rng(41)
+    vals = np.unique(ref[fin])
+    x = np.concatenate([rng.standard_normal(4000) * 40, rng.standard_normal(1000) * 1e-3,
+                        (vals[:-1] + vals[1:]) / 2]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    assert np.array_equal(OF.e4m3_encode(x.astype(np.float64)),
+                          torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+    hand = [(448.0, 0x7E), (464.0, 0x7E), (-464.0, 0xFE), (2.0 ** -9, 0x01), (2.0 ** -10, 0x00),
+            (3 * 2.0 ** -10, 0x02), (1.0625, 0x38), (1.0625 + 2 ** -10, 0x39)]
+    for v, c in hand:
+        assert OF.e4m3_encode(np.array([v]))[0] == c, (v, c)
+    assert np.isnan(OF.e4m3_decode(OF.e4m3_encode(np.array([465.0]))))[0]
+
+
+def check_fwht():
+    """The float32 butterflies equal the Sylvester Hadamard matrix (scipy) on
+    integer rows (exact), applying them twice gives d times the input, and
+    turning q and k by H(s * .) multiplies every q.k by d (fp64)."""
+    import scipy.linalg
+    rng = np.random.default_rng(43)
+    for d in (2, 4, 8, 64, 128):
+        x = rng.integers(-7, 8, size=(5, d)).astype(np.float64)
+        H = scipy.linalg.hadamard(d)
+        assert np.array_equal(OF.fwht_f32(x), x @ H)
+        assert np.array_equal(OF.fwht_f32(OF.fwht_f32(x)), d * x)
+    s = rng.choice([-1.0, 1.0], size=128)
+    q = rng.integers(-4, 5, size=(6, 128)).astype(np.float64)
+    k = rng.integers(-4, 5, size=(9, 128)).astype(np.float64)
+    assert np.array_equal(OF.fwht_f32(q * s) @ OF.fwht_f32(k * s).T, 128 * (q @ k.T))
+
+
+def check_quantize_blocks():
+    """Every block's largest magnitude becomes +-448 and its scale is
+    amax / 448 (float32); dequantised values stay within the E4M3 rounding of
+    the (turned) input: 2^-4 relative for codes >= 2^-6, 2^-10 * scale below
+    (plus the float32 product); a zero block has scale 0 and codes 0; the last
+    block may be short; a block of rows scaled by 2^k gets a scale 2^k times
+    larger and the same codes."""
+    rng = np.random.default_rng(47)
+    x = rng.standard_normal((2, 150, 3, 128)).astype(np.float32).astype(np.float64)
+    x[1, 64:128, 2] = 0.0
+    x[0, 64:128, 1] = x[0, 0:64, 1] * 8.0
+    for signs in (None, rng.choice([-1.0, 1.0], size=128)):
+        codes, scales = OF.quantize_blocks(x, signs)
+        assert scales.shape == (2, 3, 3)
+        xt = x if signs is None else OF.fwht_f32(x * signs)
+        dq = OF.dequantize(codes, scales)
+        for b in range(2):
+            for h in range(3):
+                for kb in range(3):
+                    blk = xt[b, 64 * kb:64 * (kb + 1), h]
+                    amax = np.max(np.abs(blk))
+                    assert scales[b, h, kb] == float(np.float32(amax) / np.float32(448.0))
+                    c = codes[b, 64 * kb:64 * (kb + 1), h]
+                    if amax == 0:
+                        assert np.all(c == 0)
+                        continue
+                    top = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
+                    assert c[top] & 0x7F == 0x7E
+        err = np.abs(dq - xt)
+        sc = OF.dequantize(np.full(codes.shape, 0x38, dtype=np.uint8), scales)  # the scale, per element
+        assert np.all(err <= (2.0 ** -4 * np.abs(xt) + 2.0 ** -10 * sc) * (1 + 2.0 ** -20))
+        if signs is None:
+            assert np.array_equal(codes[0, 64:128, 1], codes[0, 0:64, 1])
+            assert scales[0, 1, 1] == 8 * scales[0, 1, 0]
+    assert np.all(OF.quantize_blocks(x, None)[0][1, 64:128, 2] == 0)
+
+
+def check_vt_layout():
+    """V^T byte order inside a 64-key block, worked by hand: position
+    p = 32 h + 16 kb + 4 g + e holds key 32 kb + 8 g + 4 h + e, so positions
+    0..3 hold keys 0..3, 4..7 keys 8..11, 16 key 32, 32 key 4, 33 key 5,
+    48 key 36; it is a bijection; the layout moves d in front of the keys and
+    pads the last block with zero codes."""
+    hand = {0: 0, 3: 3, 4: 8, 7: 11, 16: 32, 31: 59, 32: 4, 33: 5, 48: 36, 63: 63}
+    for p, key in hand.items():
+        assert OF.vt_key_of_position(p) == key, (p, key)
+    assert sorted(OF.vt_key_of_position(p) for p in range(64)) == list(range(64))
+    rng = np.random.default_rng(53)
+    c = rng.integers(1, 255, size=(2, 100, 3, 8)).astype(np.uint8)
+    vt = OF.vt_layout(c)
+    assert vt.shape == (2, 3, 8, 128)
+    for k0 in (0, 64):
+        for p in range(64):
+            key = k0 + OF.vt_key_of_position(p)
+            if key < 100:
+                assert np.array_equal(vt[:, :, :, k0 + p], c[:, key].transpose(0, 1, 2))
+            else:
+                assert np.all(vt[:, :, :, k0 + p] == 0)
+
+
+def check_fp8_attention_and_bound():
+    """Turning Q and K by the Hadamard matrix leaves exact attention unchanged
+    once the scale is divided by d (fp64, no quantisation); attention on the quantised operands
+    stays close to the unquantised one; and a slow model of the kernel's
+    probability rounding (tests/fp8_tile_model.py) stays within
+    fp8_out_bound everywhere, causal and not, with and without the turn,
+    with a V block of zeros and V tiles of very different scales."""
+    from fp8_tile_model import fp8_tiled_attention
+    rng = np.random.default_rng(59)
+    B, N, Hq, Hkv, d = 1, 150, 2, 1, 128
+    q = rng.standard_normal((B, N, Hq, d))
+    k = rng.standard_normal((B, N, Hkv, d))
+    v = rng.standard_normal((B, N, Hkv, d))
+    v[0, 64:128] *= 0.01
+    v[0, 128:] = 0.0
+    s = rng.choice([-1.0, 1.0], size=d)
+    o1, l1 = OA.attention_ref(q, k, v, causal=True, softmax_scale=d ** -0.5)
+    import scipy.linalg
+    H = scipy.linalg.hadamard(d).astype(np.float64)
+    o2, l2 = OA.attention_ref((q * s) @ H, (k * s) @ H, v, causal=True, softmax_scale=d ** -0.5 / d)
+    assert np.max(np.abs(o1 - o2)) < 1e-9 and np.max(np.abs(l1 - l2)) < 1e-9
+    for causal in (True, False):
+        for inc in (False, True):
+            sg = s if inc else None
+            qc, qs = OF.quantize_blocks(q, sg)
+            kc, ks = OF.quantize_blocks(k, sg)
+            vc, vs = OF.quantize_blocks(v, None)
+            kw = dict(causal=causal, softmax_scale=d ** -0.5, incoherent=inc)
+            ref, lse = OF.attention_fp8_ref(qc, kc, vc, qs, ks, vs, **kw)
+            o, _ = OA.attention_ref(q, k, v, causal=causal, softmax_scale=d ** -0.5)
+            assert np.max(np.abs(ref - o)) < 0.2
+            bound = OF.fp8_out_bound(qc, kc, vc, qs, ks, vs, **kw)
+            rows = [0, 1, 63, 64, 100, 149]
+            model = fp8_tiled_attention(qc, kc, vc, qs, ks, vs, rows=rows, **kw)
+            err = np.abs(model[:, rows] - ref[:, rows])
+            assert np.all(err <= bound[:, rows] * (1 + 1e-9) + 1e-12), float(np.max(err - bound[:, rows]))
+            assert np.max(bound[:, rows]) < 0.2
+
+
 ALL_CHECKS = [
     check_two_tiles_printed, check_tile_states, check_tiles_and_shifts, check_masked_rows,
     check_causal_masks_printed, check_gqa_printed, check_rows_sum_to_one, check_closed_forms,
@@ -841,4 +991,5 @@ ALL_CHECKS = [
     check_bwd_gqa_and_packing, check_window_forms, check_window_brute_force, check_paged_prefill,
     check_round_bf16, check_rotary_quarter_turns, check_rotary_relative_position, check_rotary_f32,
     check_append, check_decode_append,
+    check_e4m3_codec, check_fwht, check_quantize_blocks, check_vt_layout, check_fp8_attention_and_bound,
 ]

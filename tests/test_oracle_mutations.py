@@ -11,6 +11,7 @@ import pytest
 
 import oracle.attention as OA
 import oracle.kvcache as OK
+import oracle.fp8 as OF
 import pins
 
 _orig_attend = OA._attend_rows
@@ -274,6 +275,97 @@ KV_MUTANTS = {
 def test_pins_catch_kvcache_mutant(name, monkeypatch):
     attr, fn = KV_MUTANTS[name]
     monkeypatch.setattr(OK, attr, fn)
+    caught = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check()
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, f"no pin catches mutant {name}"
+
+
+# ---- FP8 forward (planted in oracle.fp8) ------------------------------------------
+
+_orig_encode = OF.e4m3_encode
+_orig_fwht = OF.fwht_f32
+_orig_quant = OF.quantize_blocks
+_orig_vtkey = OF.vt_key_of_position
+_orig_dequant = OF.dequantize
+_orig_fp8_attn = OF.attention_fp8_ref
+
+
+def _encode_rounding(fn):
+    def enc(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        e = np.clip(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6, 8)
+        step = 2.0 ** (e - 3)
+        return _orig_encode(np.sign(x) * fn(a / step) * step)
+    return enc
+
+
+def _fwht_sign_swapped(x):
+    y = np.array(x, dtype=np.float32)
+    d = y.shape[-1]
+    h = 1
+    while h < d:
+        y = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :], y[..., 1, :] = a + b, b - a
+        y = y.reshape(y.shape[:-3] + (d,))
+        h *= 2
+    return y.astype(np.float64)
+
+
+def _fwht_missing_stage(x):
+    y = np.array(x, dtype=np.float32)
+    d = y.shape[-1]
+    h = 2
+    while h < d:
+        y = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :], y[..., 1, :] = a + b, a - b
+        y = y.reshape(y.shape[:-3] + (d,))
+        h *= 2
+    return y.astype(np.float64)
+
+
+def _quant_scale_256(x, signs=None, block=64):
+    codes, scales = _orig_quant(np.asarray(x, dtype=np.float64) * (256.0 / 448.0), signs, block)
+    return codes, scales * (448.0 / 256.0)
+
+
+def _quant_ignores_signs(x, signs=None, block=64):
+    return _orig_quant(x, None, block)
+
+
+def _dequant_off_by_one_row(codes, scales, block=64):
+    vals = OF.e4m3_decode(codes)
+    n = vals.shape[1]
+    sc = np.asarray(scales, dtype=np.float64)
+    rows = np.minimum((np.arange(n) + 1) // block, sc.shape[2] - 1)
+    return vals * sc[:, :, rows].transpose(0, 2, 1)[..., None]
+
+
+FP8_MUTANTS = {
+    "e4m3_truncates": ("e4m3_encode", _encode_rounding(np.trunc)),
+    "e4m3_ties_away": ("e4m3_encode", _encode_rounding(lambda t: np.floor(t + 0.5))),
+    "fwht_sign_swapped": ("fwht_f32", _fwht_sign_swapped),
+    "fwht_missing_stage": ("fwht_f32", _fwht_missing_stage),
+    "quantize_scale_256": ("quantize_blocks", _quant_scale_256),
+    "quantize_ignores_signs": ("quantize_blocks", _quant_ignores_signs),
+    "vt_halves_and_blocks_swapped": ("vt_key_of_position",
+                                     lambda p: 32 * (p // 32) + 8 * ((p % 16) // 4) + 4 * ((p % 32) // 16) + p % 4),
+    "dequantize_block_off_by_one_row": ("dequantize", _dequant_off_by_one_row),
+    "fp8_attention_scale_not_divided": ("attention_fp8_ref",
+                                        lambda *a, **kw: _orig_fp8_attn(*a, **dict(kw, incoherent=False))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_pins_catch_fp8_mutant(name, monkeypatch):
+    attr, fn = FP8_MUTANTS[name]
+    monkeypatch.setattr(OF, attr, fn)
     caught = []
     for check in pins.ALL_CHECKS:
         try:
