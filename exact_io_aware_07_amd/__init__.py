@@ -53,6 +53,10 @@ _SIGNATURES = {
     "attn_decode_combine": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "attn_decode_kvcache": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                              _I, _I, _I, _F, _P, _P, _P, _P, _P, _P], _I),
+    "attn_fp8_quantize": ([_P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "attn_fp8_codes_bytes": ([_I, _I, _I, _I, _I], ctypes.c_size_t),
+    "attn_fp8_num_blocks": ([_I], _I),
+    "attn_fwd_fp8": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "attn_decode_num_splits": ([_I, _I], _I),
     "attn_decode_default_chunk": ([_I, _I, _I, _I], _I),
     "attn_decode_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
@@ -457,6 +461,88 @@ def attn_decode_kvcache(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_
             _ptr(lse), _stream(stream, dev))
     _check(st)
     return out, lse, q_rot
+
+
+def attn_fp8_num_blocks(seqlen):
+    return lib().attn_fp8_num_blocks(int(seqlen))
+
+
+def attn_fp8_quantize(x, *, signs=None, layout="rows", codes=None, scales=None, stream=None):
+    """Block-quantise x [B, N, H, 128] bf16 to E4M3 codes (uint8) and float32
+    block scales [B, H, ceil(N / 64)].  signs: int8 [128] of +-1 to turn the
+    rows first (Q and K), or None.  layout "rows": codes [B, N, H, 128];
+    "vt": codes [B, H, 128, Np] in the V^T layout attn_fwd_fp8 reads."""
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev)
+    if x.dim() != 4:
+        raise ValueError("x must be [B, N, H, d]")
+    B, N, H, d = x.shape
+    lay = {"rows": 0, "vt": 1}[layout]
+    nb = attn_fp8_num_blocks(N)
+    shape = (B, N, H, d) if lay == 0 else (B, H, d, 64 * nb)
+    if codes is None:
+        codes = torch.empty(shape, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((B, H, nb), dtype=torch.float32, device=dev)
+    _need(codes, "codes", torch.uint8, dev)
+    _need(scales, "scales", torch.float32, dev)
+    if tuple(codes.shape) != shape or tuple(scales.shape) != (B, H, nb):
+        raise ValueError("codes/scales have the wrong shape")
+    if signs is not None:
+        _need(signs, "signs", torch.int8, dev)
+        if tuple(signs.shape) != (d,):
+            raise ValueError("signs must be [head_dim]")
+    with torch.cuda.device(dev):
+        st = lib().attn_fp8_quantize(_ptr(x), _ptr(signs), B, N, H, d, lay, _ptr(codes), _ptr(scales),
+                                     _stream(stream, dev))
+    _check(st)
+    return codes, scales
+
+
+def attn_fwd_fp8(q_codes, k_codes, v_codes_t, q_scales, k_scales, v_scales, *, causal, softmax_scale,
+                 incoherent, out=None, lse=None, return_lse=True, stream=None):
+    """Attention forward on attn_fp8_quantize's codes: q [B, Nq, Hq, 128] and
+    k [B, Nk, Hkv, 128] in the row layout, v in the V^T layout
+    [B, Hkv, 128, Np].  Returns (out [B, Nq, Hq, 128] bf16, lse [B, Hq, Nq])."""
+    dev = q_codes.device
+    for t, n in ((q_codes, "q_codes"), (k_codes, "k_codes"), (v_codes_t, "v_codes_t")):
+        _need(t, n, torch.uint8, dev)
+    for t, n in ((q_scales, "q_scales"), (k_scales, "k_scales"), (v_scales, "v_scales")):
+        _need(t, n, torch.float32, dev)
+    if q_codes.dim() != 4 or k_codes.dim() != 4 or v_codes_t.dim() != 4:
+        raise ValueError("codes must be 4-d")
+    B, Nq, Hq, d = q_codes.shape
+    Bk, Nk, Hkv, dk = k_codes.shape
+    nbq, nbk = attn_fp8_num_blocks(Nq), attn_fp8_num_blocks(Nk)
+    if (Bk != B or dk != d or tuple(v_codes_t.shape) != (B, Hkv, d, 64 * nbk)
+            or tuple(q_scales.shape) != (B, Hq, nbq) or tuple(k_scales.shape) != (B, Hkv, nbk)
+            or tuple(v_scales.shape) != (B, Hkv, nbk)):
+        raise ValueError("inconsistent FP8 operand shapes")
+    if out is None:
+        out = torch.empty((B, Nq, Hq, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = lib().attn_fwd_fp8(_ptr(q_codes), _ptr(k_codes), _ptr(v_codes_t), _ptr(q_scales), _ptr(k_scales),
+                                _ptr(v_scales), B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), int(bool(incoherent)),
+                                float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream, dev))
+    _check(st)
+    return out, lse
+
+
+def attn_fp8_forward(q, k, v, *, causal, softmax_scale, signs=None, stream=None):
+    """Quantise bf16 q, k, v ([B, N, H, 128]) and run attn_fwd_fp8: Q and K turned
+    by `signs` (incoherent processing) when given.  Returns (out, lse)."""
+    qc, qs = attn_fp8_quantize(q, signs=signs, layout="rows", stream=stream)
+    kc, ks = attn_fp8_quantize(k, signs=signs, layout="rows", stream=stream)
+    vc, vs = attn_fp8_quantize(v, layout="vt", stream=stream)
+    return attn_fwd_fp8(qc, kc, vc, qs, ks, vs, causal=causal, softmax_scale=softmax_scale,
+                        incoherent=signs is not None, stream=stream)
 
 
 def attn_check_cu_seqlens(cu_seqlens, total, max_seqlen):

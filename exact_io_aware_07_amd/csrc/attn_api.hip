@@ -442,6 +442,98 @@ attn_status_t attn_decode_kvcache(const void* q, const void* k_new, const void* 
     return hip_status(attn::launch_decode_combine(c, head_dim, s), "attn_decode_kvcache combine launch");
 }
 
+int attn_fp8_num_blocks(int seqlen) {
+    if (seqlen <= 0) return 0;
+    return (int)(((long)seqlen + 63) / 64);
+}
+
+size_t attn_fp8_codes_bytes(int batch, int seqlen, int num_heads, int head_dim, int layout) {
+    if (batch < 1 || seqlen < 1 || num_heads < 1 || head_dim < 1 || (layout != 0 && layout != 1)) return 0;
+    const size_t n = layout == 0 ? (size_t)seqlen : (size_t)attn_fp8_num_blocks(seqlen) * 64;
+    return (size_t)batch * n * num_heads * head_dim;
+}
+
+attn_status_t attn_fp8_quantize(const void* x, const int8_t* signs, int batch, int seqlen, int num_heads,
+                                int head_dim, int layout, void* codes, float* scales, void* stream) {
+    if (!x || !codes || !scales) return fail(ATTN_ERR_NULL, "x, codes and scales must be non-NULL");
+    if (batch < 1 || seqlen < 1 || num_heads < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d seqlen=%d num_heads=%d", batch, seqlen,
+                    num_heads);
+    if (layout != 0 && layout != 1) return fail(ATTN_ERR_SHAPE, "layout must be 0 (rows) or 1 (V^T)");
+    if (head_dim != 128) return fail(ATTN_ERR_UNSUPPORTED, "FP8 path: head_dim must be 128 (got %d)", head_dim);
+    const size_t xb = (size_t)batch * seqlen * num_heads * head_dim * 2;
+    const size_t cb = attn_fp8_codes_bytes(batch, seqlen, num_heads, head_dim, layout);
+    const size_t sb = (size_t)batch * num_heads * attn_fp8_num_blocks(seqlen) * 4;
+    if (overlap(codes, cb, x, xb) || overlap(codes, cb, signs, (size_t)head_dim) || overlap(scales, sb, x, xb) ||
+        overlap(scales, sb, signs, (size_t)head_dim) || overlap(codes, cb, scales, sb))
+        return fail(ATTN_ERR_ALIAS, "codes/scales overlap an input or each other");
+    attn::Fp8QuantParams p{};
+    p.x = static_cast<const uint16_t*>(x);
+    p.signs = signs;
+    p.codes = static_cast<uint8_t*>(codes);
+    p.scales = scales;
+    p.batch = batch;
+    p.n = seqlen;
+    p.heads = num_heads;
+    return hip_status(attn::launch_fp8_quant(p, layout == 1, static_cast<hipStream_t>(stream)),
+                      "attn_fp8_quantize launch");
+}
+
+attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void* v_codes_t,
+                           const float* q_scales, const float* k_scales, const float* v_scales, int batch,
+                           int seqlen_q, int seqlen_k, int num_heads_q, int num_heads_kv, int head_dim,
+                           int causal, int incoherent, float softmax_scale, void* out, float* lse,
+                           void* stream) {
+    if (!q_codes || !k_codes || !v_codes_t || !q_scales || !k_scales || !v_scales || !out)
+        return fail(ATTN_ERR_NULL, "codes, scales and out must be non-NULL");
+    if (batch < 1 || seqlen_q < 1 || seqlen_k < 1 || num_heads_q < 1 || num_heads_kv < 1)
+        return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d seqlen_q=%d seqlen_k=%d num_heads_q=%d "
+                    "num_heads_kv=%d", batch, seqlen_q, seqlen_k, num_heads_q, num_heads_kv);
+    if (num_heads_q % num_heads_kv)
+        return fail(ATTN_ERR_SHAPE, "num_heads_kv=%d does not divide num_heads_q=%d", num_heads_kv,
+                    num_heads_q);
+    if ((causal != 0 && causal != 1) || (incoherent != 0 && incoherent != 1))
+        return fail(ATTN_ERR_SHAPE, "causal and incoherent must be 0 or 1");
+    if (head_dim != 128) return fail(ATTN_ERR_UNSUPPORTED, "FP8 path: head_dim must be 128 (got %d)", head_dim);
+    attn_status_t st = check_scale(softmax_scale);
+    if (st != ATTN_OK) return st;
+    const size_t ob = (size_t)batch * seqlen_q * num_heads_q * head_dim * 2;
+    const size_t lb = (size_t)batch * num_heads_q * seqlen_q * 4;
+    const size_t qb = attn_fp8_codes_bytes(batch, seqlen_q, num_heads_q, head_dim, 0);
+    const size_t kb = attn_fp8_codes_bytes(batch, seqlen_k, num_heads_kv, head_dim, 0);
+    const size_t vb = attn_fp8_codes_bytes(batch, seqlen_k, num_heads_kv, head_dim, 1);
+    const size_t qsb = (size_t)batch * num_heads_q * attn_fp8_num_blocks(seqlen_q) * 4;
+    const size_t ksb = (size_t)batch * num_heads_kv * attn_fp8_num_blocks(seqlen_k) * 4;
+    const void* ins[6] = {q_codes, k_codes, v_codes_t, q_scales, k_scales, v_scales};
+    const size_t inb[6] = {qb, kb, vb, qsb, ksb, ksb};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(out, ob, ins[i], inb[i]) || overlap(lse, lb, ins[i], inb[i]))
+            return fail(ATTN_ERR_ALIAS, "out/lse overlap an input");
+    if (overlap(out, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "out and lse overlap");
+    if (128L * attn_fp8_num_blocks(seqlen_k) * 64 > 0xffffffffL)
+        return fail(ATTN_ERR_UNSUPPORTED, "seqlen_k too large for 32-bit tile offsets");
+    attn::Fp8FwdParams p{};
+    p.q = static_cast<const uint8_t*>(q_codes);
+    p.k = static_cast<const uint8_t*>(k_codes);
+    p.vt = static_cast<const uint8_t*>(v_codes_t);
+    p.q_scale = q_scales;
+    p.k_scale = k_scales;
+    p.v_scale = v_scales;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.batch = batch;
+    p.nq = seqlen_q;
+    p.nk = seqlen_k;
+    p.hq = num_heads_q;
+    p.hkv = num_heads_kv;
+    p.np = attn_fp8_num_blocks(seqlen_k) * 64;
+    p.nbq = attn_fp8_num_blocks(seqlen_q);
+    p.nbk = attn_fp8_num_blocks(seqlen_k);
+    p.scale = incoherent ? softmax_scale / (float)head_dim : softmax_scale;
+    return hip_status(attn::launch_fwd_fp8(p, causal != 0, static_cast<hipStream_t>(stream)),
+                      "attn_fwd_fp8 launch");
+}
+
 int attn_decode_num_splits(int max_seqlen_k, int chunk_tokens) {
     if (max_seqlen_k <= 0 || chunk_tokens <= 0) return 0;
     return (int)(((long)max_seqlen_k + chunk_tokens - 1) / chunk_tokens);

@@ -1,0 +1,409 @@
+// FP8 forward pass: block quantisation with incoherent processing, and the
+// attention kernel on E4M3 operands (gfx950, head_dim 128).
+//
+// "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)",
+// "FlashAttention-3": FP8 with one scale per block and incoherent processing
+// (a random orthogonal transform spreads outliers before quantisation).
+// "Flash Attention: A Complete Architectural Autopsy", "FP8 Path and
+// Quantization": each tile's scale comes from its absolute maximum, scores
+// are formed from the FP8 operands and dequantised to fp32 for the softmax,
+// and V tiles are quantised the same way.
+//
+// Quantisation runs as its own HBM-bound pass (one read of the bf16 tensor,
+// one write of the codes) rather than inside the attention kernel: there the
+// vector ALUs already limit the softmax, and a tile scale needs the whole
+// tile's maximum before any of it can be converted.
+//
+// Formats (shared by both kernels):
+//   codes   E4M3 ("fn": bias 7, max 448, no infinities), round to nearest even
+//   blocks  64 consecutive rows of one (sequence, head); scale = amax / 448,
+//           code = E4M3(x * (448 / amax)) with the product rounded to float32;
+//           a zero block has scale 0 and codes 0
+//   turn    x -> H (s * x) along d for Q and K: unnormalised Walsh-Hadamard
+//           butterflies in float32, stage h = 1, 2, 4, ..., 64, the pair
+//           (x[i], x[i+h]), i & h == 0, becoming (x[i] + x[i+h], x[i] - x[i+h]);
+//           scores of turned operands are d times the original ones
+//   Q, K    codes [B, N, H, 128] (row layout)
+//   V       codes [B, H, 128, Np] (V^T layout, Np = N rounded up to 64): inside
+//           every 64-key block, byte p = 32 h + 16 kb + 4 g + e holds key
+//           32 kb + 8 g + 4 h + e, the order in which a lane holds the keys of
+//           a score tile; padding keys are zero codes
+//   scales  float32 [B, H, ceil(N / 64)]
+
+#include "attn_tile.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kFp8D = 128;
+constexpr int kFp8Block = 64;
+constexpr float kE4M3Max = 448.0f;
+
+// D[32x32] += A[32x64] * B[64x32] on E4M3 operands (v_mfma_f32_32x32x64_f8f6f4,
+// format 0 for both): lane l holds 32 bytes of row l % 32 of A and of column
+// l % 32 of B; byte j of lane half h = l / 32 is one k index, the same for A
+// and B (probed on the GPU), so the products pair byte (h, j) of A with byte
+// (h, j) of B.  The result layout is the one of the 32x32x16 bf16 product.
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Two E4M3 codes (round to nearest even) of lo, hi into bytes 0-1 (hi_word
+// false) or 2-3 (true) of `old`.
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float lo, float hi, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, (int)old, HI_WORD);
+}
+
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+    return x;
+}
+
+// Position, inside its 64-key block of a V^T row, of key k (0..63).
+__device__ __forceinline__ uint32_t vt_pos_of_key(uint32_t k) {
+    const uint32_t kb = k >> 5, g = (k >> 3) & 3u, h = (k >> 2) & 1u, e = k & 3u;
+    return 32u * h + 16u * kb + 4u * g + e;
+}
+
+// ---- quantisation ----------------------------------------------------------------
+// One workgroup (256 threads) per (64-row block, head, sequence).  A row of
+// 128 values is held by 16 lanes, 8 consecutive values each; a wave covers 4
+// rows per pass and the workgroup 16, so 4 passes cover the block.
+template <bool VT>
+__global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
+#pragma clang fp contract(off)
+    __shared__ float wmax[4];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? kFp8D * kFp8Block : 16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nblk = (p.n + kFp8Block - 1) / kFp8Block;
+    const int kb = blockIdx.x % nblk;
+    const int bh = blockIdx.x / nblk;
+    const int h = bh % p.heads, b = bh / p.heads;
+    const int j = lane & 15;                 // 8-value chunk of the row
+    const int rsub = wave * 4 + (lane >> 4); // row within a pass
+
+    float v[4][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int n = kb * kFp8Block + 16 * pass + rsub;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (n < p.n) raw = load16(p.x + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[pass][2 * e] = __uint_as_float(raw[e] << 16);
+            v[pass][2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+        }
+        if (p.signs != nullptr) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[pass][e] *= (float)p.signs[8 * j + e];  // exact: +-1
+            // in-lane stages h = 1, 2, 4
+#pragma unroll
+            for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((e & hs) == 0) {
+                        const float a = v[pass][e], c = v[pass][e + hs];
+                        v[pass][e] = a + c;
+                        v[pass][e + hs] = a - c;
+                    }
+            // cross-lane stages h = 8, 16, 32, 64: partner lane j ^ (h / 8)
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                const bool low = (j & m) == 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float mine = v[pass][e];
+                    const float other = __shfl_xor(mine, m, 64);
+                    v[pass][e] = low ? mine + other : other - mine;
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[pass][e]));
+    }
+    amax = wave_max_f(amax);
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const bool zero = !(amax > 0.0f);
+    const float inv = zero ? 0.0f : kE4M3Max / amax;
+    if (tid == 0) p.scales[(long)bh * nblk + kb] = zero ? 0.0f : amax / kE4M3Max;
+
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+        const int r = 16 * pass + rsub;
+        const int n = kb * kFp8Block + r;
+        uint32_t lo = 0u, hi = 0u;
+        if (!zero && n < p.n) {  // padding rows are code 0 (a turned zero row can hold -0)
+            lo = cvt_fp8x2<false>(v[pass][0] * inv, v[pass][1] * inv, 0u);
+            lo = cvt_fp8x2<true>(v[pass][2] * inv, v[pass][3] * inv, lo);
+            hi = cvt_fp8x2<false>(v[pass][4] * inv, v[pass][5] * inv, 0u);
+            hi = cvt_fp8x2<true>(v[pass][6] * inv, v[pass][7] * inv, hi);
+        }
+        if constexpr (!VT) {
+            if (n < p.n)
+                *reinterpret_cast<u32x2*>(p.codes + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j) =
+                    u32x2{lo, hi};
+        } else {
+            const uint32_t pos = vt_pos_of_key((uint32_t)r);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tile[(8 * j + e) * kFp8Block + pos] = (uint8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
+        }
+    }
+    if constexpr (VT) {
+        __syncthreads();
+        const int np = nblk * kFp8Block;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i;        // 16-byte chunk of the 128 x 64 tile
+            const int dd = c >> 2, q = c & 3;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(tile + dd * kFp8Block + 16 * q);
+            *reinterpret_cast<u32x4*>(p.codes + ((long)bh * kFp8D + dd) * np + (long)kb * kFp8Block + 16 * q) = w;
+        }
+    }
+}
+
+hipError_t launch_fp8_quant(const Fp8QuantParams& p, bool vt, hipStream_t s) {
+    const long nblk = (p.n + kFp8Block - 1) / kFp8Block;
+    const long grid = nblk * p.batch * p.heads;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (vt)
+        hipLaunchKernelGGL(attn_fp8_quant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL(attn_fp8_quant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---- attention -----------------------------------------------------------------------
+// The workgroup shape of the bf16 forward (8 waves x 32 query rows, 64-key
+// tiles, two LDS stages filled by LDS-DMA, scores formed transposed so a lane
+// owns a query row).  Per tile and wave: S^T = K Q^T in 4 MFMAs (2 key blocks x
+// 2 d steps of 64) and O^T += V^T P^T in 4 (one per 32-row d block, all 64 keys
+// at once).  The lane's 32 probabilities are rounded to E4M3 in register order,
+// which is the key order of the V^T layout, so they are the B operand as they
+// stand.  Differences from the bf16 kernel's softmax: the running maximum is
+// exact (raised whenever a tile's maximum exceeds it), so probabilities are
+// <= 1 before scaling; they are multiplied by 256 * s_v(t) / max_t s_v(t)
+// (folded into the exponent), which puts the V tile scale into P and keeps
+// the E4M3 values <= 256; the row sum is kept from the unrounded values.
+template <bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8_kernel(Fp8FwdParams p) {
+    constexpr int NW = 8, BR = NW * 32, BC = 64;
+    constexpr uint32_t K_BYTES = BC * kFp8D, STAGE = 2 * K_BYTES;
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int BH = p.batch * p.hq;
+    const int bid = blockIdx.x;
+    int qt, bh;
+    if ((BH & 7) == 0) {
+        const int hpx = BH >> 3, x = bid & 7, kk = bid >> 3;
+        qt = p.n_qtiles - 1 - kk / hpx;
+        bh = x * hpx + kk % hpx;
+    } else {
+        qt = p.n_qtiles - 1 - bid / BH;
+        bh = bid % BH;
+    }
+    const int b = bh / p.hq, hq = bh % p.hq;
+    const int kvh = hq / (p.hq / p.hkv);
+    const int Nq = p.nq, Nk = p.nk;
+    const int q0 = qt * BR;
+    if (q0 >= Nq) return;
+
+    const long shift = (long)Nk - Nq;
+    auto hi_of = [&](int i) __attribute__((always_inline)) {
+        if (!CAUSAL) return Nk - 1;
+        const long hh = i + shift;
+        return (int)(hh < Nk - 1 ? hh : Nk - 1);
+    };
+    const int last_row = min(q0 + BR, Nq) - 1;
+    const int t_end = hi_of(last_row) < 0 ? 0 : hi_of(last_row) / BC + 1;
+
+    const int wr0 = q0 + wave * 32;
+    const bool wave_rows = wr0 < Nq;
+    const int w_last_row = min(wr0 + 32, Nq) - 1;
+    const int w_hi_max = hi_of(w_last_row), w_hi_min = hi_of(wr0);
+
+    const uint32_t stride_k = (uint32_t)(p.hkv * kFp8D);  // bytes between key rows
+    const uint8_t* kbase = p.k + ((long)b * Nk * p.hkv + kvh) * kFp8D;
+    const uint8_t* vtbase = p.vt + ((long)b * p.hkv + kvh) * kFp8D * (long)p.np;
+    const float* ks_row = p.k_scale + ((long)b * p.hkv + kvh) * p.nbk;
+    const float* vs_row = p.v_scale + ((long)b * p.hkv + kvh) * p.nbk;
+
+    auto issue_tile = [&](int t, uint32_t st) __attribute__((always_inline)) {
+        const int key0 = t * BC;
+        const int nvalid = Nk - key0;
+        const uint32_t nrec = nvalid > 0 ? (uint32_t)(nvalid < BC ? nvalid : BC) * stride_k : 0u;
+        const u32x4 rk = rsrc_words(kbase + (long)key0 * stride_k, nrec);
+        const uint32_t krow = 8 * wave + (lane >> 3), kc = lane & 7;
+        dma16(rk, st + 1024 * wave, krow * stride_k + ((kc ^ swz<8>(krow)) * 16));
+        const u32x4 rv = rsrc_words(vtbase + key0, 127u * (uint32_t)p.np + (uint32_t)BC);
+        const uint32_t vrow = 16 * wave + (lane >> 2), vc = lane & 3;
+        dma16(rv, st + K_BYTES + 1024 * wave, vrow * (uint32_t)p.np + ((vc ^ swz<4>(vrow)) * 16));
+    };
+
+    // Q^T fragments (B operand): lane half h holds d = 64 s + 32 h .. + 31 of its row.
+    const int row = wr0 + l32;
+    i32x8 qf[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+        if (row < Nq) {
+            const uint8_t* qrow = p.q + (((long)b * Nq + row) * p.hq + hq) * kFp8D + 64 * s + 32 * h;
+            a = *reinterpret_cast<const u32x4*>(qrow);
+            c = *reinterpret_cast<const u32x4*>(qrow + 16);
+        }
+        qf[s] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+    }
+    const float s_q = row < Nq ? p.q_scale[((long)b * p.hq + hq) * p.nbq + row / kFp8Block] : 0.0f;
+    float svmax = 0.0f;
+    for (int i = lane; i < p.nbk; i += 64) svmax = fmaxf(svmax, vs_row[i]);
+    svmax = wave_max_f(svmax);
+    const float vref = svmax > 0.0f ? svmax : 1.0f;
+    const float c2q = p.scale * kLog2e * s_q;
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    float m_run = -INFINITY, l_part = 0.0f;
+
+    if (t_end > 0) issue_tile(0, lds_addr(stage0));
+    wait_vmem();
+    __syncthreads();
+
+    auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
+        const char* ks = cur;
+        const char* vs = cur + K_BYTES;
+        if (t + 1 < t_end) issue_tile(t + 1, lds_addr(nxt));
+        const int k0 = t * BC;
+        const bool active = wave_rows && k0 <= w_hi_max;
+        if (active) {
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const uint32_t kr = 32 * kb + l32;
+                    const uint32_t c0 = 4 * s + 2 * h;
+                    const u32x4 a0 = lds_read16(ks, kr * kFp8D + ((c0 ^ swz<8>(kr)) * 16));
+                    const u32x4 a1 = lds_read16(ks, kr * kFp8D + (((c0 + 1) ^ swz<8>(kr)) * 16));
+                    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    sacc[kb] = mfma_fp8(a, qf[s], sacc[kb]);
+                }
+            // scores of the turned, dequantised operands in log2 units: S * c2t
+            const float c2t = fmaxf(c2q * ks_row[t], 1.17549435e-38f);
+            if (k0 + BC - 1 > w_hi_min || k0 + BC > Nk) {
+                const int hi = hi_of(row);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (k0 + score_key(kb, r, lane) > hi) sacc[kb][r] = -INFINITY;
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+            mx = pair_max(mx) * c2t;
+            const bool raise = mx > m_run;
+            if (__builtin_amdgcn_ballot_w64(raise && m_run != -INFINITY)) {
+                const float alpha = (raise && m_run != -INFINITY) ? exp2f(m_run - mx) : 1.0f;
+                l_part *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            if (raise) m_run = mx;
+            // V tile scale folded into P: P' = p * 256 * s_v(t) / max s_v
+            const float sv = vs_row[t];
+            const float lg = 8.0f + ((sv > 0.0f && svmax > 0.0f) ? __log2f(sv) - __log2f(svmax) : 0.0f);
+            const float inv_g = exp2f(-lg);
+            const float sh = (m_run == -INFINITY) ? 0.0f : m_run - lg;
+            float rs = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c2t, -sh));
+                    sacc[kb][r] = e;
+                    rs += e;
+                }
+            l_part = __builtin_fmaf(rs, inv_g, l_part);
+            i32x8 pb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int kb = i >> 2, r0 = 4 * (i & 3);
+                uint32_t w = cvt_fp8x2<false>(sacc[kb][r0], sacc[kb][r0 + 1], 0u);
+                w = cvt_fp8x2<true>(sacc[kb][r0 + 2], sacc[kb][r0 + 3], w);
+                pb[i] = (int)w;
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const uint32_t vr = 32 * db + l32;
+                const u32x4 a0 = lds_read16(vs, vr * BC + (((2 * h) ^ swz<4>(vr)) * 16));
+                const u32x4 a1 = lds_read16(vs, vr * BC + (((2 * h + 1) ^ swz<4>(vr)) * 16));
+                const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                oacc[db] = mfma_fp8(a, pb, oacc[db]);
+            }
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+    for (int t = 0; t < t_end; t += 2) {
+        step(t, stage0, stage1);
+        if (t + 1 < t_end) step(t + 1, stage1, stage0);
+    }
+
+    const float l_tot = pair_sum(l_part);
+    if (row < Nq) {
+        const float inv = l_tot > 0.0f ? vref / (256.0f * l_tot) : 0.0f;
+        uint16_t* orow = p.out + (((long)b * Nq + row) * p.hq + hq) * kFp8D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
+                           pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g + 4 * h) = w;
+            }
+        if (p.lse != nullptr && h == 0)
+            p.lse[((long)b * p.hq + hq) * Nq + row] =
+                l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+}
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p0, bool causal, hipStream_t s) {
+    Fp8FwdParams p = p0;
+    p.n_qtiles = (p.nq + 255) / 256;
+    const long grid = (long)p.n_qtiles * p.batch * p.hq;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    if (causal)
+        hipLaunchKernelGGL(attn_fwd_fp8_kernel<true>, dim3((unsigned)grid), dim3(512), 0, s, p);
+    else
+        hipLaunchKernelGGL(attn_fwd_fp8_kernel<false>, dim3((unsigned)grid), dim3(512), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn

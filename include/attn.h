@@ -139,6 +139,75 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v,
                           void* out, float* lse, void* stream);
 
 /*
+ * attn_fp8_quantize -- block quantisation to FP8 (E4M3) with optional
+ * incoherent processing ("FlashAttention-3 and PagedAttention: IO-Aware
+ * Attention Kernels (2026)", "FlashAttention-3": FP8 with one scale per block
+ * and a random orthogonal transform that spreads outliers first; "Flash
+ * Attention: A Complete Architectural Autopsy", "FP8 Path and Quantization":
+ * a tile's scale comes from its absolute maximum).
+ *
+ *   x       [batch, seqlen, num_heads, head_dim] bf16 (finite values)
+ *   signs   NULL, or int8 [head_dim] of +1/-1: each row is first turned to
+ *           H (s * x), H the unnormalised Sylvester-ordered Walsh-Hadamard
+ *           matrix, computed in float32 by butterflies (stage h = 1, 2, 4, ...,
+ *           head_dim/2; the pair (x[i], x[i+h]) with i & h == 0 becomes
+ *           (x[i] + x[i+h], x[i] - x[i+h])).  Give Q and K the same signs and
+ *           V none; attn_fwd_fp8's `incoherent` then divides the scale by d.
+ *   layout  0: codes [batch, seqlen, num_heads, head_dim] (for Q and K);
+ *           1: codes [batch, num_heads, head_dim, Np], Np = 64 *
+ *           attn_fp8_num_blocks(seqlen) (for V): inside every 64-key block,
+ *           byte p = 32 h + 16 kb + 4 g + e (0 <= h, kb < 2, g, e < 4) of a row
+ *           holds key 32 kb + 8 g + 4 h + e; padding keys hold code 0.
+ *   codes   uint8 E4M3 ("fn": bias 7, max 448, no infinities) codes, round to
+ *           nearest even; attn_fp8_codes_bytes(...) bytes, written
+ *   scales  float32 [batch, num_heads, attn_fp8_num_blocks(seqlen)], written:
+ *           for each block of 64 consecutive rows of one (sequence, head),
+ *           amax = max |x| (after the turn), scale = amax / 448 and code =
+ *           E4M3(x * (448 / amax)) with the product rounded to float32; a
+ *           block of zeros gets scale 0 and codes 0.  value ~ code * scale.
+ * Requirements: head_dim == 128 (ATTN_ERR_UNSUPPORTED), positive counts,
+ * layout 0 or 1 (ATTN_ERR_SHAPE); codes and scales must not overlap x, signs
+ * or each other (ATTN_ERR_ALIAS).
+ */
+attn_status_t attn_fp8_quantize(const void* x, const int8_t* signs, int batch, int seqlen, int num_heads,
+                                int head_dim, int layout, void* codes, float* scales, void* stream);
+
+/* Bytes of attn_fp8_quantize's codes for a layout (0 for invalid sizes), and
+ * the number of 64-row blocks of a sequence (ceil(seqlen / 64), 0 if <= 0). */
+size_t attn_fp8_codes_bytes(int batch, int seqlen, int num_heads, int head_dim, int layout);
+int attn_fp8_num_blocks(int seqlen);
+
+/*
+ * attn_fwd_fp8 -- attention forward on FP8 operands from attn_fp8_quantize
+ * (dense batches; "Flash Attention: A Complete Architectural Autopsy", "FP8
+ * Path and Quantization": scores are formed from the FP8 operands and
+ * dequantised to fp32 for the softmax; the online softmax is that of
+ * attn_fwd).
+ *
+ *   q_codes, k_codes  layout 0 codes of Q [batch, seqlen_q, num_heads_q, 128]
+ *                     and K [batch, seqlen_k, num_heads_kv, 128]
+ *   v_codes_t         layout 1 codes of V [batch, num_heads_kv, 128, Np]
+ *   q/k/v_scales      their block scales
+ *   incoherent        1 if Q and K were turned (same signs): the scores of the
+ *                     turned operands are d times the original ones, so
+ *                     softmax_scale / 128 is applied
+ *   out, lse          as attn_fwd in dense mode (bf16 out, float32 lse in
+ *                     nats, lse may be NULL); causal masks align bottom-right
+ * The probabilities are rounded to E4M3 for the P V product, after scaling by
+ * 256 * s_v / max(s_v) of the V tile (which folds the V scales into P); the
+ * running maximum is exact so they are at most 1 before that scaling, and the
+ * row sums use the unrounded values.  Results equal exact attention on the
+ * dequantised operands within the error of that rounding (2^-4 relative per
+ * probability, 2^-10 absolute below 2^-6).
+ * Requirements: head_dim == 128; others as attn_fwd.
+ */
+attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void* v_codes_t,
+                           const float* q_scales, const float* k_scales, const float* v_scales, int batch,
+                           int seqlen_q, int seqlen_k, int num_heads_q, int num_heads_kv, int head_dim,
+                           int causal, int incoherent, float softmax_scale, void* out, float* lse,
+                           void* stream);
+
+/*
  * attn_bwd -- gradients of attn_fwd by recomputation.
  *
  * From the forward's saved q, k, v, out and lse and the upstream gradient

@@ -180,10 +180,28 @@ def attention_fp8_ref(q_codes, k_codes, v_codes, q_scales, k_scales, v_scales, *
     return _A.attention_ref(q, k, v, causal=causal, softmax_scale=scale)
 
 
+def _bound_block(Q, K, V, Vcode, vs_row, scale, keep):
+    """Bound of fp8_out_bound for query rows Q [n, d] against one K/V head
+    (K, V, Vcode [Nk, d]; vs_row the head's V block scales; keep [n, Nk])."""
+    smax = float(np.max(vs_row)) if len(vs_row) else 0.0
+    g = np.where((vs_row > 0) & (smax > 0), vs_row / (smax if smax > 0 else 1.0), 1.0)
+    g_key = g[np.arange(K.shape[0]) // BLOCK]
+    vref = smax if smax > 0 else 1.0
+    S = np.where(keep, scale * (Q @ K.T), -np.inf)
+    m = np.max(S, axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.where(keep, np.exp(S - m), 0.0)
+    L = np.sum(p, axis=1, keepdims=True)
+    Ls = np.where(L > 0, L, 1.0)
+    sub = keep & (256.0 * g_key[None, :] * p < 2.0 ** -6)
+    return 2.0 ** -4 * ((p / Ls) @ np.abs(V)) + 2.0 ** -10 * vref / 256.0 / Ls * (sub @ np.abs(Vcode))
+
+
 def fp8_out_bound(q_codes, k_codes, v_codes, q_scales, k_scales, v_scales, *, causal, softmax_scale,
-                  incoherent):
-    """Per-element bound [B, Nq, Hq, d] on |out_gpu - out_ref| from rounding the
-    probabilities to E4M3.
+                  incoherent, rows=None):
+    """Per-element bound on |out_gpu - out_ref| from rounding the
+    probabilities to E4M3: [B, Nq, Hq, d], or [len(rows), d] for `rows`, a
+    list of (seq, q_head, i).
 
     The kernel keeps the exact running maximum m and rounds P'_j =
     p_j * 256 * g_t to E4M3, where p_j = exp(s_j - m) <= 1 and g_t =
@@ -203,25 +221,19 @@ def fp8_out_bound(q_codes, k_codes, v_codes, q_scales, k_scales, v_scales, *, ca
     Nk, Hkv = k.shape[1], k.shape[2]
     scale = softmax_scale / d if incoherent else softmax_scale
     kvmap = _A.kv_head_for_queries(Hq, Hkv)
-    bound = np.zeros((B, Nq, Hq, d))
     vs = np.asarray(v_scales, dtype=np.float64)
+    full_keep = _A.causal_keep(Nq, Nk) if causal else np.ones((Nq, Nk), dtype=bool)
+    if rows is not None:
+        out = np.zeros((len(rows), d))
+        for n, (b, h, i) in enumerate(rows):
+            kvh = kvmap[h]
+            out[n] = _bound_block(q[b, i:i + 1, h, :], k[b, :, kvh, :], v[b, :, kvh, :], vcode[b, :, kvh, :],
+                                  vs[b, kvh], scale, full_keep[i:i + 1])[0]
+        return out
+    bound = np.zeros((B, Nq, Hq, d))
     for b in range(B):
         for h in range(Hq):
             kvh = kvmap[h]
-            smax = np.max(vs[b, kvh]) if vs.shape[2] else 0.0
-            g = np.where((vs[b, kvh] > 0) & (smax > 0), vs[b, kvh] / (smax if smax > 0 else 1.0), 1.0)
-            g_key = g[np.arange(Nk) // BLOCK]
-            vref = smax if smax > 0 else 1.0
-            S = scale * (q[b, :, h, :] @ k[b, :, kvh, :].T)
-            keep = _A.causal_keep(Nq, Nk) if causal else np.ones((Nq, Nk), dtype=bool)
-            S = np.where(keep, S, -np.inf)
-            m = np.max(S, axis=1, keepdims=True)
-            m = np.where(np.isfinite(m), m, 0.0)
-            p = np.where(keep, np.exp(S - m), 0.0)
-            L = np.sum(p, axis=1, keepdims=True)
-            Ls = np.where(L > 0, L, 1.0)
-            w = p / Ls
-            sub = keep & (256.0 * g_key[None, :] * p < 2.0 ** -6)
-            bound[b, :, h, :] = (2.0 ** -4 * (w @ np.abs(v[b, :, kvh, :]))
-                                 + 2.0 ** -10 * vref / 256.0 / Ls * (sub @ np.abs(vcode[b, :, kvh, :])))
+            bound[b, :, h, :] = _bound_block(q[b, :, h, :], k[b, :, kvh, :], v[b, :, kvh, :], vcode[b, :, kvh, :],
+                                             vs[b, kvh], scale, full_keep)
     return bound

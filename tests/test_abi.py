@@ -161,6 +161,52 @@ def test_decode_kvcache_rejects(kw, code):
     assert kvc(**kw) == code
 
 
+def fp8q(**kw):
+    a = dict(x=_at(0), signs=NULL, batch=2, n=100, h=3, d=128, layout=0, codes=_at(1), scales=_at(2))
+    a.update(kw)
+    return ea.lib().attn_fp8_quantize(a["x"], a["signs"], a["batch"], a["n"], a["h"], a["d"], a["layout"],
+                                      a["codes"], a["scales"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=NULL), 1), (dict(codes=NULL), 1), (dict(scales=NULL), 1),
+    (dict(batch=0), 2), (dict(n=0), 2), (dict(h=-1), 2), (dict(layout=2), 2),
+    (dict(d=64), 3), (dict(d=256, layout=1), 3),
+    (dict(codes=_at(0)), 5), (dict(scales=ctypes.c_void_p(0x1000000 + 100)), 5), (dict(signs=_at(1)), 5),
+    (dict(scales=ctypes.c_void_p(0x2000000 + 64)), 5),
+])
+def test_fp8_quantize_rejects(kw, code):
+    assert fp8q(**kw) == code
+
+
+def fp8f(**kw):
+    a = dict(q=_at(0), k=_at(1), v=_at(2), qs=_at(3), ks=_at(4), vs=_at(5), batch=1, nq=100, nk=120, hq=4,
+             hkv=2, d=128, causal=1, inc=1, scale=0.1, out=_at(6), lse=_at(7))
+    a.update(kw)
+    return ea.lib().attn_fwd_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["batch"], a["nq"], a["nk"],
+                                 a["hq"], a["hkv"], a["d"], a["causal"], a["inc"], a["scale"], a["out"], a["lse"],
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), 1), (dict(v=NULL), 1), (dict(vs=NULL), 1), (dict(out=NULL), 1),
+    (dict(batch=0), 2), (dict(nk=0), 2), (dict(hq=6, hkv=4), 2), (dict(causal=2), 2), (dict(inc=-1), 2),
+    (dict(d=64), 3), (dict(scale=0.0), 4), (dict(scale=float("inf")), 4),
+    (dict(out=_at(0)), 5), (dict(lse=_at(5)), 5), (dict(lse=ctypes.c_void_p(0x7000000 + 8)), 5),
+])
+def test_fwd_fp8_rejects(kw, code):
+    assert fp8f(**kw) == code
+
+
+def test_fp8_sizes():
+    lib = ea.lib()
+    assert lib.attn_fp8_num_blocks(1) == 1 and lib.attn_fp8_num_blocks(64) == 1 and lib.attn_fp8_num_blocks(65) == 2
+    assert lib.attn_fp8_num_blocks(0) == 0
+    assert lib.attn_fp8_codes_bytes(2, 100, 3, 128, 0) == 2 * 100 * 3 * 128
+    assert lib.attn_fp8_codes_bytes(2, 100, 3, 128, 1) == 2 * 3 * 128 * 128
+    assert lib.attn_fp8_codes_bytes(2, 100, 3, 128, 2) == 0
+
+
 DQ = ctypes.c_void_p(0x60000000)
 DK = ctypes.c_void_p(0x70000000)
 DV = ctypes.c_void_p(0x78000000)

@@ -1,0 +1,130 @@
+"""FP8 forward on the HIP path vs the CPU oracle (needs an MI355X).
+
+Quantisation is byte work: codes and scales must equal the oracle's bit for
+bit (oracle.fp8.quantize_blocks, which takes its rounding decisions in float32
+as the GPU does).  Attention on the codes is compared with exact fp64
+attention on the dequantised operands: every output element within the bound
+of oracle.fp8.fp8_out_bound (the error of rounding probabilities to E4M3), with
+5% slack for float32 arithmetic, plus 2^-8 of the value for the bf16 output
+rounding and 1e-5; lse within 1e-3; rows with no key exactly 0 and -inf.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_07_amd as ea
+import oracle
+import oracle.fp8 as OF
+import workloads as W
+from test_parity_gpu import to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def np_bf16(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("N,H,turn,layout", [(130, 3, False, "rows"), (130, 3, True, "rows"), (200, 2, False, "vt"),
+                                             (64, 1, True, "vt"), (1, 2, False, "rows"), (65, 2, True, "vt"),
+                                             (300, 2, True, "rows")],
+                         ids=lambda x: str(x))
+def test_quantize_bit_exact(N, H, turn, layout):
+    x = np_bf16((2, N, H, 128), seed=N + H)
+    if N >= 128:
+        x[0, 64:128, 0] = 0.0            # a zero block
+        x[1, 64:128, 1 % H] *= 1e-3      # a quiet block
+        x[1, 70, 0, 5] = 300.0           # an outlier
+    signs = W.hadamard_signs(128, seed=N) if turn else None
+    codes, scales = ea.attn_fp8_quantize(x.to(DEV), signs=None if signs is None else signs.to(DEV), layout=layout)
+    torch.cuda.synchronize()
+    ref_c, ref_s = OF.quantize_blocks(to64(x), None if signs is None else signs.numpy().astype(np.float64))
+    if layout == "vt":
+        ref_c = OF.vt_layout(ref_c)
+    got = codes.cpu().numpy()
+    assert got.shape == ref_c.shape
+    assert np.array_equal(got, ref_c), f"{int((got != ref_c).sum())} codes differ"
+    assert np.array_equal(scales.cpu().numpy().astype(np.float64), ref_s)
+
+
+def check_fp8(case, causal, turn, seed, rows=None):
+    """Run the FP8 path on a dense case and compare with the oracle (all rows, or sampled rows)."""
+    d = 128
+    scale = d ** -0.5
+    signs = W.hadamard_signs(d, seed) if turn else None
+    q, k, v = (case[x] for x in "qkv")
+    sd = None if signs is None else signs.to(DEV)
+    qc, qs = ea.attn_fp8_quantize(q.to(DEV), signs=sd)
+    kc, ks = ea.attn_fp8_quantize(k.to(DEV), signs=sd)
+    vc, vs = ea.attn_fp8_quantize(v.to(DEV), layout="vt")
+    out, lse = ea.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, causal=causal, softmax_scale=scale, incoherent=turn)
+    torch.cuda.synchronize()
+    sg = None if signs is None else signs.numpy().astype(np.float64)
+    rq, rqs = OF.quantize_blocks(to64(q), sg)
+    rk, rks = OF.quantize_blocks(to64(k), sg)
+    rv, rvs = OF.quantize_blocks(to64(v), None)
+    # the operands the kernel read are the oracle's, bit for bit
+    assert np.array_equal(qc.cpu().numpy(), rq) and np.array_equal(kc.cpu().numpy(), rk)
+    assert np.array_equal(vc.cpu().numpy(), OF.vt_layout(rv))
+    kw = dict(causal=causal, softmax_scale=scale, incoherent=turn)
+    o, l = to64(out), to64(lse)
+    if rows is None:
+        ref_o, ref_l = OF.attention_fp8_ref(rq, rk, rv, rqs, rks, rvs, **kw)
+        bound = OF.fp8_out_bound(rq, rk, rv, rqs, rks, rvs, **kw)
+        got_o, got_l = o, l
+    else:
+        sc = scale / d if turn else scale
+        ref_o, ref_l = oracle.attention_rows(OF.dequantize(rq, rqs), OF.dequantize(rk, rks), OF.dequantize(rv, rvs),
+                                             rows, causal=causal, softmax_scale=sc)
+        bound = OF.fp8_out_bound(rq, rk, rv, rqs, rks, rvs, rows=rows, **kw)
+        got_o = np.array([o[b, i, h] for b, h, i in rows])
+        got_l = np.array([l[b, h, i] for b, h, i in rows])
+    err = np.abs(got_o - ref_o)
+    tol = 1.05 * bound + 2.0 ** -8 * np.abs(ref_o) + 1e-5
+    assert np.all(np.isfinite(got_o)), "non-finite output"
+    assert np.all(err <= tol), f"max err/tol {np.max(err / tol):.3f}, max err {err.max():.3e}"
+    empty = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(got_l), empty)
+    assert np.max(np.abs(got_l[~empty] - ref_l[~empty]), initial=0.0) <= 1e-3
+    if empty.any():
+        rows_empty = empty if rows is not None else empty.transpose(0, 2, 1)  # lse [B, H, N] -> out [B, N, H]
+        assert np.all(got_o[rows_empty] == 0)
+    return float(np.mean(err)), float(np.mean(bound))
+
+
+SHAPES = [
+    # (B, Nq, Nk, Hq, Hkv, causal, incoherent)
+    (1, 128, 128, 2, 2, True, True),
+    (2, 200, 333, 4, 2, True, False),
+    (1, 300, 300, 4, 1, False, True),
+    (1, 65, 700, 2, 2, True, True),
+    (1, 700, 65, 2, 1, True, True),     # leading rows see no key
+    (1, 1, 900, 8, 2, True, False),
+    (1, 513, 1030, 2, 2, False, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_fp8_small(shape):
+    B, Nq, Nk, Hq, Hkv, causal, turn = shape
+    case = W.dense_case(B, Nq, Nk, Hq, Hkv, 128, seed=Nq + 3 * Nk)
+    check_fp8(case, causal, turn, seed=Nq)
+
+
+def test_fwd_fp8_key_outliers_and_quiet_tiles():
+    """K with 1% of rows x3 (the GQA workload's recipe) and a V tile 1000x quieter than the rest."""
+    case = W.dense_case(1, 256, 640, 4, 2, 128, seed=77, k_outlier_frac=0.01)
+    case["v"][0, 128:192] = (case["v"][0, 128:192].float() * 1e-3).to(torch.bfloat16)
+    check_fp8(case, True, True, seed=5)
+    check_fp8(case, True, False, seed=5)
+
+
+def test_fwd_fp8_prefill_workload_sampled():
+    """The causal MHA prefill workload (B=4, H=16, N=4096, d=128) with incoherent processing:
+    all codes bit for bit, sampled rows against the oracle."""
+    case = W.config_case("mha_causal_b4_h16_n4096_d128", device="cpu")
+    rows = [(0, 0, 0), (0, 5, 63), (1, 15, 64), (2, 7, 2047), (3, 3, 4095), (3, 15, 1000), (1, 0, 4000)]
+    check_fp8(case, True, True, seed=9, rows=rows)

@@ -8,5 +8,6 @@ from .gen import (  # noqa: F401
     decode_case,
     append_case,
     rotary_tables,
+    hadamard_signs,
     config_case,
 )

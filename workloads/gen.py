@@ -168,6 +168,13 @@ def append_case(seqlens, Hq, Hkv, d, seed, *, device="cpu", poison=False, extra_
     return case
 
 
+def hadamard_signs(d, seed, device="cpu"):
+    """int8 [d] of +-1 drawn from a seeded generator: the random sign vector of
+    incoherent processing (an input the caller chooses)."""
+    g = _gen(seed, "cpu")
+    return (torch.randint(0, 2, (d,), generator=g, dtype=torch.int64) * 2 - 1).to(torch.int8).to(device)
+
+
 def config_case(name, *, device="cpu", d=None, poison=False):
     """Materialise one of CONFIGS (d overrides the head dim of the varlen case)."""
     c = CONFIGS[name]
