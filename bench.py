@@ -238,6 +238,55 @@ def time_decode_kvcache(ea, W, dev, props, stream, torch, reps=20):
             "workload": DECODE + " with one appended token per request, rotary over all 128 features"}
 
 
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
+
+
+def time_fp8(ea, W, pc, stream, torch, reps=20):
+    """FP8 forward on the prefill workload, timed apart from the step: the three
+    quantisation passes (Q and K turned by seeded random signs, V into the V^T
+    layout) and attn_fwd_fp8, each bracketed by events.  FLOPs as the bf16
+    metric (the same attention)."""
+    signs = W.hadamard_signs(pc["d"], 9, device=pc["q"].device)
+    q, k, v = pc["q"], pc["k"], pc["v"]
+    qc, qs = ea.attn_fp8_quantize(q, signs=signs, stream=stream)
+    kc, ks = ea.attn_fp8_quantize(k, signs=signs, stream=stream)
+    vc, vs = ea.attn_fp8_quantize(v, layout="vt", stream=stream)
+    out = torch.empty_like(q)
+    lse = torch.empty((pc["B"], pc["Hq"], pc["Nq"]), dtype=torch.float32, device=q.device)
+
+    def quant():
+        ea.attn_fp8_quantize(q, signs=signs, codes=qc, scales=qs, stream=stream)
+        ea.attn_fp8_quantize(k, signs=signs, codes=kc, scales=ks, stream=stream)
+        ea.attn_fp8_quantize(v, layout="vt", codes=vc, scales=vs, stream=stream)
+
+    def attn():
+        ea.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, causal=pc["causal"], softmax_scale=pc["scale"], incoherent=True,
+                        out=out, lse=lse, stream=stream)
+
+    for _ in range(3):
+        quant()
+        attn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        quant()
+        e[1].record(stream)
+        attn()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    a_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    flops = prefill_flops(pc)
+    tf = flops / (a_ms * 1e-3) / 1e12
+    qbytes = 3 * 3 * q.numel()  # read bf16 (2 B), write codes (1 B), three tensors
+    return {"kernel_ms_mean": round(a_ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+            "quantize_ms_mean": round(q_ms, 4), "quantize_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            "end_to_end_tflops": round(flops / ((q_ms + a_ms) * 1e-3) / 1e12, 2),
+            "workload": PREFILL + ", E4M3, 64-row block scales, Q and K turned by a random-sign Hadamard transform"}
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
     import numpy as np
@@ -297,6 +346,8 @@ def main():
                     help="skip the separately timed attn_bwd leg (not part of the step)")
     ap.add_argument("--no-kvcache", action="store_true",
                     help="skip the separately timed attn_decode_kvcache leg (not part of the step)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the separately timed FP8 forward leg (not part of the step)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for counter scaling)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -386,6 +437,7 @@ def main():
     wall = time.perf_counter() - t0
     bwd = None if args.no_backward else time_backward(ea, pc, out, lse, stream, torch)
     kvc = None if args.no_kvcache else time_decode_kvcache(ea, W, dev, props, stream, torch)
+    fp8 = None if args.no_fp8 else time_fp8(ea, W, pc, stream, torch)
     pre = [e[0].elapsed_time(e[1]) for e in events]
     spl = [e[1].elapsed_time(e[2]) for e in events]
     cmb = [e[2].elapsed_time(e[3]) for e in events]
@@ -444,6 +496,8 @@ def main():
         rec["backward"] = bwd
     if kvc is not None:
         rec["decode_kvcache"] = kvc
+    if fp8 is not None:
+        rec["fp8_forward"] = fp8
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pc)
     print(json.dumps(rec), flush=True)
