@@ -70,9 +70,40 @@ __device__ __forceinline__ uint32_t vt_pos_of_key(uint32_t k) {
 }
 
 // ---- quantisation ----------------------------------------------------------------
-// One workgroup (256 threads) per (64-row block, head, sequence).  A row of
-// 128 values is held by 16 lanes, 8 consecutive values each; a wave covers 4
-// rows per pass and the workgroup 16, so 4 passes cover the block.
+// Value of lane (this lane ^ M) within the 16-lane group of a row, by DPP:
+// M = 1, 2 are quad permutes, M = 8 rotates the 16-lane row by 8, and M = 4
+// mirrors each half-row (i -> 7 - i) and then reverses each quad (i -> i ^ 3),
+// which together map i to i ^ 4.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+    const int v = __float_as_int(x);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+    else if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false));
+    else {
+        const int m = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);           // row_half_mirror
+        return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false));  // quad_perm [3,2,1,0]
+    }
+}
+
+// One cross-lane butterfly stage of the turn: the lane holding x[i] (bit M of
+// its chunk index clear) keeps x[i] + x[i+h], its partner x[i] - x[i+h].
+template <int M>
+__device__ __forceinline__ void xstage(float (&v)[4][8], bool low) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float mine = v[i][e];
+            const float other = lane_xor<M>(mine);
+            v[i][e] = low ? mine + other : other - mine;
+        }
+}
+
+// One workgroup (256 threads) per (64-row block, head, sequence).  Thread t
+// holds rows 4 (t / 16) .. + 3 of the block, values 8 (t % 16) .. + 7 of each:
+// a row's 128 values lie on 16 consecutive lanes (the butterflies' partners),
+// and four consecutive rows are four consecutive keys of a V^T word.
 template <bool VT>
 __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
 #pragma clang fp contract(off)
@@ -83,49 +114,57 @@ __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
     const int kb = blockIdx.x % nblk;
     const int bh = blockIdx.x / nblk;
     const int h = bh % p.heads, b = bh / p.heads;
-    const int j = lane & 15;                 // 8-value chunk of the row
-    const int rsub = wave * 4 + (lane >> 4); // row within a pass
+    const int j = tid & 15;          // 8-value chunk of the rows
+    const int r0 = 4 * (tid >> 4);   // first of this thread's four rows
 
-    float v[4][8];
-    float amax = 0.0f;
+    u32x4 raw[4];
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        const int n = kb * kFp8Block + 16 * pass + rsub;
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (n < p.n) raw = load16(p.x + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j);
+    for (int i = 0; i < 4; ++i) {
+        const int n = kb * kFp8Block + r0 + i;
+        raw[i] = u32x4{0u, 0u, 0u, 0u};
+        if (n < p.n) raw[i] = load16(p.x + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j);
+    }
+    float sg[8];
+    if (p.signs != nullptr) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(p.signs + 8 * j);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sg[e] = (float)(int8_t)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+    }
+    float v[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            v[pass][2 * e] = __uint_as_float(raw[e] << 16);
-            v[pass][2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+            v[i][2 * e] = __uint_as_float(raw[i][e] << 16);
+            v[i][2 * e + 1] = __uint_as_float(raw[i][e] & 0xffff0000u);
         }
-        if (p.signs != nullptr) {
+    if (p.signs != nullptr) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[pass][e] *= (float)p.signs[8 * j + e];  // exact: +-1
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] *= sg[e];  // exact: +-1
             // in-lane stages h = 1, 2, 4
 #pragma unroll
             for (int hs = 1; hs < 8; hs <<= 1)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     if ((e & hs) == 0) {
-                        const float a = v[pass][e], c = v[pass][e + hs];
-                        v[pass][e] = a + c;
-                        v[pass][e + hs] = a - c;
+                        const float a = v[i][e], c = v[i][e + hs];
+                        v[i][e] = a + c;
+                        v[i][e + hs] = a - c;
                     }
-            // cross-lane stages h = 8, 16, 32, 64: partner lane j ^ (h / 8)
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1) {
-                const bool low = (j & m) == 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float mine = v[pass][e];
-                    const float other = __shfl_xor(mine, m, 64);
-                    v[pass][e] = low ? mine + other : other - mine;
-                }
-            }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[pass][e]));
+        // cross-lane stages h = 8, 16, 32, 64: partner chunk j ^ (h / 8)
+        xstage<1>(v, (j & 1) == 0);
+        xstage<2>(v, (j & 2) == 0);
+        xstage<4>(v, (j & 4) == 0);
+        xstage<8>(v, (j & 8) == 0);
     }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
     amax = wave_max_f(amax);
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
@@ -134,29 +173,44 @@ __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
     const float inv = zero ? 0.0f : kE4M3Max / amax;
     if (tid == 0) p.scales[(long)bh * nblk + kb] = zero ? 0.0f : amax / kE4M3Max;
 
+    // codes of row i: lo = values 0..3, hi = values 4..7 (byte e = value e)
+    uint32_t lo[4], hi[4];
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-        const int r = 16 * pass + rsub;
-        const int n = kb * kFp8Block + r;
-        uint32_t lo = 0u, hi = 0u;
-        if (!zero && n < p.n) {  // padding rows are code 0 (a turned zero row can hold -0)
-            lo = cvt_fp8x2<false>(v[pass][0] * inv, v[pass][1] * inv, 0u);
-            lo = cvt_fp8x2<true>(v[pass][2] * inv, v[pass][3] * inv, lo);
-            hi = cvt_fp8x2<false>(v[pass][4] * inv, v[pass][5] * inv, 0u);
-            hi = cvt_fp8x2<true>(v[pass][6] * inv, v[pass][7] * inv, hi);
-        }
-        if constexpr (!VT) {
-            if (n < p.n)
-                *reinterpret_cast<u32x2*>(p.codes + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j) =
-                    u32x2{lo, hi};
-        } else {
-            const uint32_t pos = vt_pos_of_key((uint32_t)r);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                tile[(8 * j + e) * kFp8Block + pos] = (uint8_t)(((e < 4 ? lo : hi) >> (8 * (e & 3))) & 0xffu);
+    for (int i = 0; i < 4; ++i) {
+        lo[i] = hi[i] = 0u;
+        if (!zero && kb * kFp8Block + r0 + i < p.n) {  // padding rows are code 0 (a turned zero row can hold -0)
+            lo[i] = cvt_fp8x2<false>(v[i][0] * inv, v[i][1] * inv, 0u);
+            lo[i] = cvt_fp8x2<true>(v[i][2] * inv, v[i][3] * inv, lo[i]);
+            hi[i] = cvt_fp8x2<false>(v[i][4] * inv, v[i][5] * inv, 0u);
+            hi[i] = cvt_fp8x2<true>(v[i][6] * inv, v[i][7] * inv, hi[i]);
         }
     }
-    if constexpr (VT) {
+    if constexpr (!VT) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = kb * kFp8Block + r0 + i;
+            if (n < p.n)
+                *reinterpret_cast<u32x2*>(p.codes + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j) =
+                    u32x2{lo[i], hi[i]};
+        }
+    } else {
+        // Rows r0 .. r0+3 are keys at positions pos .. pos+3 of the V^T block:
+        // transpose the 4x4 bytes of each half so that word e holds value e of
+        // the four rows, and write one word per value.
+        const uint32_t pos = vt_pos_of_key((uint32_t)r0);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint32_t* a = half ? hi : lo;
+            const uint32_t t0 = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);  // a0[0] a1[0] a0[1] a1[1]
+            const uint32_t t1 = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);  // a0[2] a1[2] a0[3] a1[3]
+            const uint32_t t2 = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
+            const uint32_t t3 = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
+            const uint32_t w[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                                   __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                *reinterpret_cast<uint32_t*>(tile + (8 * j + 4 * half + e) * kFp8Block + pos) = w[e];
+        }
         __syncthreads();
         const int np = nblk * kFp8Block;
 #pragma unroll
