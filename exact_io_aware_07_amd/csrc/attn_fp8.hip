@@ -40,6 +40,13 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kFp8D = 128;
 constexpr int kFp8Block = 64;
 constexpr float kE4M3Max = 448.0f;
+// The attention kernel's shift is raised only when a tile's maximum exceeds it
+// by more than kFp8Rescale (log2 units), so probabilities are <= 2^kFp8Rescale;
+// they are multiplied by 2^kFp8PScale before rounding to E4M3, which keeps the
+// rounded values <= 256 (E4M3 max 448) and puts a probability 2^-12 below the
+// shift at the bottom of the normal range.
+constexpr float kFp8Rescale = 2.0f;
+constexpr float kFp8PScale = 6.0f;
 
 // D[32x32] += A[32x64] * B[64x32] on E4M3 operands (v_mfma_f32_32x32x64_f8f6f4,
 // format 0 for both): lane l holds 32 bytes of row l % 32 of A and of column
@@ -242,11 +249,11 @@ hipError_t launch_fp8_quant(const Fp8QuantParams& p, bool vt, hipStream_t s) {
 // 2 d steps of 64) and O^T += V^T P^T in 4 (one per 32-row d block, all 64 keys
 // at once).  The lane's 32 probabilities are rounded to E4M3 in register order,
 // which is the key order of the V^T layout, so they are the B operand as they
-// stand.  Differences from the bf16 kernel's softmax: the running maximum is
-// exact (raised whenever a tile's maximum exceeds it), so probabilities are
-// <= 1 before scaling; they are multiplied by 256 * s_v(t) / max_t s_v(t)
-// (folded into the exponent), which puts the V tile scale into P and keeps
-// the E4M3 values <= 256; the row sum is kept from the unrounded values.
+// stand.  Differences from the bf16 kernel's softmax: the shift is raised when
+// a tile's maximum exceeds it by more than kFp8Rescale, so probabilities are
+// <= 4; they are multiplied by 64 * s_v(t) / max_t s_v(t) (folded into the
+// exponent), which puts the V tile scale into P and keeps the E4M3 values
+// <= 256; the row sum is kept from the unrounded values.
 template <bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8_kernel(Fp8FwdParams p) {
@@ -378,7 +385,7 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
             mx = pair_max(mx) * c2t;
-            const bool raise = mx > m_run;
+            const bool raise = mx > m_run + kFp8Rescale;
             if (__builtin_amdgcn_ballot_w64(raise && m_run != -INFINITY)) {
                 const float alpha = (raise && m_run != -INFINITY) ? exp2f(m_run - mx) : 1.0f;
                 l_part *= alpha;
@@ -388,9 +395,9 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
                     for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
             }
             if (raise) m_run = mx;
-            // V tile scale folded into P: P' = p * 256 * s_v(t) / max s_v
+            // V tile scale folded into P: P' = p * 64 * s_v(t) / max s_v
             const float sv = vs_row[t];
-            const float lg = 8.0f + ((sv > 0.0f && svmax > 0.0f) ? __log2f(sv) - __log2f(svmax) : 0.0f);
+            const float lg = kFp8PScale + ((sv > 0.0f && svmax > 0.0f) ? __log2f(sv) - __log2f(svmax) : 0.0f);
             const float inv_g = exp2f(-lg);
             const float sh = (m_run == -INFINITY) ? 0.0f : m_run - lg;
             float rs = 0.0f;
@@ -431,7 +438,7 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
 
     const float l_tot = pair_sum(l_part);
     if (row < Nq) {
-        const float inv = l_tot > 0.0f ? vref / (256.0f * l_tot) : 0.0f;
+        const float inv = l_tot > 0.0f ? vref / (exp2f(kFp8PScale) * l_tot) : 0.0f;
         uint16_t* orow = p.out + (((long)b * Nq + row) * p.hq + hq) * kFp8D;
 #pragma unroll
         for (int db = 0; db < 4; ++db)

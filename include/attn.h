@@ -194,9 +194,10 @@ int attn_fp8_num_blocks(int seqlen);
  *   out, lse          as attn_fwd in dense mode (bf16 out, float32 lse in
  *                     nats, lse may be NULL); causal masks align bottom-right
  * The probabilities are rounded to E4M3 for the P V product, after scaling by
- * 256 * s_v / max(s_v) of the V tile (which folds the V scales into P); the
- * running maximum is exact so they are at most 1 before that scaling, and the
- * row sums use the unrounded values.  Results equal exact attention on the
+ * 64 * s_v / max(s_v) of the V tile (which folds the V scales into P); the
+ * softmax shift is raised only when a tile's maximum exceeds it by more than
+ * 2 in log2 units, so they are at most 4 before that scaling, and the row
+ * sums use the unrounded values.  Results equal exact attention on the
  * dequantised operands within the error of that rounding (2^-4 relative per
  * probability, 2^-10 absolute below 2^-6).
  * Requirements: head_dim == 128; others as attn_fwd.

@@ -31,8 +31,10 @@ Readings (the pages fix none of these details):
 
 Attention on the quantised operands (attention_fp8_ref) is the exact fp64
 definition on the dequantised Q, K, V; the kernel also rounds the
-probabilities to E4M3 before the P V product, an approximation whose error is
-bounded by fp8_out_bound.
+probabilities to E4M3 before the P V product (scaled by P_SCALE and the V tile
+scales; its shift trails the running maximum by at most RESCALE_LOG2, the
+conditional rescaling of "Deep Dive - FlashAttention", "FA1 through FA4 retune
+the same IO idea"), an approximation whose error is bounded by fp8_out_bound.
 """
 import numpy as np
 
@@ -40,6 +42,8 @@ from . import attention as _A
 
 E4M3_MAX = 448.0
 BLOCK = 64
+P_SCALE = 64.0      # probabilities are multiplied by this (and s_v / max s_v) before rounding
+RESCALE_LOG2 = 2.0  # the kernel's shift may trail the running maximum by up to this (log2 units)
 
 
 def e4m3_decode(codes):
@@ -193,8 +197,8 @@ def _bound_block(Q, K, V, Vcode, vs_row, scale, keep):
     p = np.where(keep, np.exp(S - m), 0.0)
     L = np.sum(p, axis=1, keepdims=True)
     Ls = np.where(L > 0, L, 1.0)
-    sub = keep & (256.0 * g_key[None, :] * p < 2.0 ** -6)
-    return 2.0 ** -4 * ((p / Ls) @ np.abs(V)) + 2.0 ** -10 * vref / 256.0 / Ls * (sub @ np.abs(Vcode))
+    sub = keep & (P_SCALE * g_key[None, :] * p < 2.0 ** -6)
+    return 2.0 ** -4 * ((p / Ls) @ np.abs(V)) + 2.0 ** -10 * vref / P_SCALE / Ls * (sub @ np.abs(Vcode))
 
 
 def fp8_out_bound(q_codes, k_codes, v_codes, q_scales, k_scales, v_scales, *, causal, softmax_scale,
@@ -203,15 +207,15 @@ def fp8_out_bound(q_codes, k_codes, v_codes, q_scales, k_scales, v_scales, *, ca
     probabilities to E4M3: [B, Nq, Hq, d], or [len(rows), d] for `rows`, a
     list of (seq, q_head, i).
 
-    The kernel keeps the exact running maximum m and rounds P'_j =
-    p_j * 256 * g_t to E4M3, where p_j = exp(s_j - m) <= 1 and g_t =
-    s_v(t) / max_t s_v(t) folds the V tile scales into P (g_t = 1 where a
-    scale is 0).  Each rounding is within 2^-4 of P'_j when P'_j >= 2^-6 and
-    within 2^-10 absolutely below, so with exact weights w_j = p_j / L:
-        |err_c| <= 2^-4 sum_j w_j |v_jc| + 2^-10 * vmax / 256 / L
-                   * sum_{j: 256 g_t p_j < 2^-6} |code(v_jc)|
-    with p_j and L taken at the row's final maximum (earlier tiles, rounded
-    under a smaller maximum, only do better).
+    The kernel rounds P'_j = exp(s_j - c) * 64 * g_t to E4M3, where c is its
+    shift (never above the running maximum, and at most RESCALE_LOG2 below
+    it, so exp(s_j - c) <= 4) and g_t = s_v(t) / max_t s_v(t) folds the V tile
+    scales into P (g_t = 1 where a scale is 0).  Each rounding is within 2^-4
+    of P'_j when P'_j >= 2^-6 and within 2^-10 absolutely below.  With the
+    exact weights w_j = p_j / L, p_j = exp(s_j - m) at the row's final maximum
+    m (c <= m, so the kernel's values and row sum are at least p_j and L):
+        |err_c| <= 2^-4 sum_j w_j |v_jc| + 2^-10 * vmax / 64 / L
+                   * sum_{j: 64 g_t p_j < 2^-6} |code(v_jc)|
     """
     q = dequantize(q_codes, q_scales)
     k = dequantize(k_codes, k_scales)
