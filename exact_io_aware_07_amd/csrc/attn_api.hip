@@ -39,6 +39,17 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
+// True if any non-null pointer is not a multiple of `a` bytes.
+template <typename... P>
+bool misaligned(uintptr_t a, P... ps) {
+    return ((ps != nullptr && (reinterpret_cast<uintptr_t>(ps) & (a - 1)) != 0) || ...);
+}
+
+attn_status_t fail_align() {
+    return fail(ATTN_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned (int32 arrays, lse, scales "
+                "and rotary tables 4-byte, FP8 signs 8-byte)");
+}
+
 attn_status_t check_scale(float s) {
     if (!isfinite(s) || !(s > 0.0f)) return fail(ATTN_ERR_SCALE, "softmax_scale must be finite and > 0 (got %g)", s);
     return ATTN_OK;
@@ -78,6 +89,8 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v, const int
                           int window_left, int window_right, float softmax_scale, void* out, float* lse,
                           void* stream) {
     if (!q || !k || !v || !out) return fail(ATTN_ERR_NULL, "q, k, v and out must be non-NULL");
+    if (misaligned(16, q, k, v, out) || misaligned(4, lse, cu_seqlens_q, cu_seqlens_k, block_table, seqlens_k))
+        return fail_align();
     const bool paged = block_table != nullptr;
     const bool varlen = cu_seqlens_q != nullptr;
     if (paged) {
@@ -167,6 +180,8 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
         return fail(ATTN_ERR_NULL, "every tensor argument of attn_bwd must be non-NULL");
+    if (misaligned(16, q, k, v, out, dout, dq, dk, dv, workspace) || misaligned(4, lse, cu_seqlens_q, cu_seqlens_k))
+        return fail_align();
     const bool varlen = cu_seqlens_q != nullptr;
     if (varlen != (cu_seqlens_k != nullptr))
         return fail(ATTN_ERR_NULL, "cu_seqlens_q and cu_seqlens_k must both be NULL or both be set");
@@ -243,6 +258,8 @@ attn_status_t attn_decode_splitkv(const void* q, const void* k_cache, const void
                                   float* lse_partial, void* stream) {
     if (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !out_partial || !lse_partial)
         return fail(ATTN_ERR_NULL, "every pointer argument of attn_decode_splitkv must be non-NULL");
+    if (misaligned(16, q, k_cache, v_cache, out_partial) || misaligned(4, block_table, seqlens_k, lse_partial))
+        return fail_align();
     if (batch < 1 || num_heads_q < 1 || num_heads_kv < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
         num_splits < 1)
         return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d num_heads_q=%d num_heads_kv=%d "
@@ -291,6 +308,7 @@ attn_status_t attn_decode_combine(const float* out_partial, const float* lse_par
                                   float* lse, void* stream) {
     if (!out_partial || !lse_partial || !seqlens_k || !out)
         return fail(ATTN_ERR_NULL, "out_partial, lse_partial, seqlens_k and out must be non-NULL");
+    if (misaligned(16, out_partial, out) || misaligned(4, lse_partial, seqlens_k, lse)) return fail_align();
     if (batch < 1 || num_heads_q < 1 || num_splits < 1)
         return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d num_heads_q=%d num_splits=%d",
                     batch, num_heads_q, num_splits);
@@ -336,6 +354,9 @@ attn_status_t attn_decode_kvcache(const void* q, const void* k_new, const void* 
                     "and out must be non-NULL");
     if (rotary_dim != 0 && (!rotary_cos || !rotary_sin || !q_rot))
         return fail(ATTN_ERR_NULL, "rotary_dim > 0 needs rotary_cos, rotary_sin and q_rot");
+    if (misaligned(16, q, k_new, v_new, k_cache, v_cache, q_rot, out_partial, out) ||
+        misaligned(4, block_table, seqlens_k, rotary_cos, rotary_sin, lse_partial, lse))
+        return fail_align();
     if (batch < 1 || num_heads_q < 1 || num_heads_kv < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
         num_splits < 1)
         return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d num_heads_q=%d num_heads_kv=%d "
@@ -456,6 +477,7 @@ size_t attn_fp8_codes_bytes(int batch, int seqlen, int num_heads, int head_dim, 
 attn_status_t attn_fp8_quantize(const void* x, const int8_t* signs, int batch, int seqlen, int num_heads,
                                 int head_dim, int layout, void* codes, float* scales, void* stream) {
     if (!x || !codes || !scales) return fail(ATTN_ERR_NULL, "x, codes and scales must be non-NULL");
+    if (misaligned(16, x, codes) || misaligned(8, signs) || misaligned(4, scales)) return fail_align();
     if (batch < 1 || seqlen < 1 || num_heads < 1)
         return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d seqlen=%d num_heads=%d", batch, seqlen,
                     num_heads);
@@ -486,6 +508,8 @@ attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void*
                            void* stream) {
     if (!q_codes || !k_codes || !v_codes_t || !q_scales || !k_scales || !v_scales || !out)
         return fail(ATTN_ERR_NULL, "codes, scales and out must be non-NULL");
+    if (misaligned(16, q_codes, k_codes, v_codes_t, out) || misaligned(4, q_scales, k_scales, v_scales, lse))
+        return fail_align();
     if (batch < 1 || seqlen_q < 1 || seqlen_k < 1 || num_heads_q < 1 || num_heads_kv < 1)
         return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d seqlen_q=%d seqlen_k=%d num_heads_q=%d "
                     "num_heads_kv=%d", batch, seqlen_q, seqlen_k, num_heads_q, num_heads_kv);

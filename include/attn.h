@@ -13,6 +13,11 @@
  * Element types: bf16 tensors are IEEE bfloat16 stored as 16-bit words;
  * lse and the decode partials are IEEE float32.  All tensors are dense and
  * row-major in the layouts documented below (no strides are accepted).
+ * Alignment: bf16, float32 partial and FP8 code tensors (and workspaces) are
+ * read and written with 16-byte vector accesses and must start on a 16-byte
+ * boundary; int32 arrays, lse, scales and rotary tables on a 4-byte one, the
+ * FP8 signs on an 8-byte one (allocations from the HIP allocator or PyTorch
+ * are).  A misaligned pointer gives ATTN_ERR_UNSUPPORTED.
  *
  * What is computed (the definition the results are checked against):
  *   for each sequence and query head h, with K/V head kvh = h / (Hq / Hkv),
@@ -43,7 +48,7 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,        /* a required pointer is NULL                               */
     ATTN_ERR_SHAPE = 2,       /* a count or length is out of range, or Hq % Hkv != 0      */
-    ATTN_ERR_UNSUPPORTED = 3, /* head_dim not in {64,128,256}, page_size != 256, bad chunk  */
+    ATTN_ERR_UNSUPPORTED = 3, /* head_dim, page size, chunk or pointer alignment not supported */
     ATTN_ERR_SCALE = 4,       /* softmax_scale is not finite or not > 0                    */
     ATTN_ERR_ALIAS = 5,       /* an output overlaps an input or the other output           */
     ATTN_ERR_HIP = 6,         /* the HIP runtime refused a launch (see attn_last_error)    */

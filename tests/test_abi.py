@@ -275,3 +275,18 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ea.attn_fwd(q, q, q, causal=False, softmax_scale=0.125)
+
+
+ODD = ctypes.c_void_p(0x10000 + 2)   # 2-byte aligned: fine for no tensor
+
+
+@pytest.mark.parametrize("call,kw", [
+    (fwd, dict(q=ODD)), (fwd, dict(out=ctypes.c_void_p(0x40000000 + 8))), (fwd, dict(lse=ctypes.c_void_p(0x50000000 + 2))),
+    (fwd_ex, dict(PAGED, bt=ODD)), (dec, dict(kc=ODD)), (dec, dict(sl=ctypes.c_void_p(0x70000 + 1))),
+    (comb, dict(po=ctypes.c_void_p(0x10000 + 4))), (bwd, dict(ws=ctypes.c_void_p(0x7c000000 + 8))),
+    (kvc, dict(q=ODD)), (kvc, dict(ROPE, cos=ctypes.c_void_p(0xB000000 + 2))), (fp8q, dict(x=ODD)),
+    (fp8q, dict(signs=ctypes.c_void_p(0x3000000 + 4))), (fp8f, dict(v=ctypes.c_void_p(0x3000000 + 8))),
+])
+def test_misaligned_pointers_rejected(call, kw):
+    """Misaligned tensors are refused before any launch (ATTN_ERR_UNSUPPORTED)."""
+    assert call(**kw) == 3
