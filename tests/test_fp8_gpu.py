@@ -104,6 +104,10 @@ SHAPES = [
     (1, 700, 65, 2, 1, True, True),     # leading rows see no key
     (1, 1, 900, 8, 2, True, False),
     (1, 513, 1030, 2, 2, False, False),
+    (1, 100, 30, 2, 2, False, True),    # fewer keys than one tile
+    (1, 100, 30, 2, 2, True, True),     # ... causal: the first 70 rows see nothing
+    (2, 64, 64, 16, 1, True, True),     # MQA, one tile
+    (1, 250, 2000, 8, 2, True, True),   # Nk >> Nq: bottom-right rows see long prefixes
 ]
 
 
