@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PREFILL = "mha_causal_b4_h16_n4096_d128"
 DECODE = "paged_decode_b64_hq32_hkv8_d128"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["attn_tile.h", "attn_fwd.hip", "attn_decode.hip", "attn_launch.h"]
+KERNEL_SOURCES = ["attn_tile.h", "attn_launch.h", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_fp8.hip"]
 
 
 def source_digest():
@@ -92,7 +92,25 @@ def load_traffic(kernel_key, digest):
     return k.get("hbm_bytes_per_launch")
 
 
-TRAFFIC_KERNELS = {"attn_fwd_kernel": "attn_fwd_kernel", "attn_decode_split_kernel": "attn_decode_split_kernel"}
+# Counter key -> substring of the rocprofv3 kernel name ("<" keeps attn_fwd_kernel
+# apart from attn_fwd_fp8_kernel).  Per-launch figures average every dispatch
+# of the run, so a kernel shared by two legs (the decode split kernel) averages
+# over both.
+TRAFFIC_KERNELS = {
+    "attn_fwd_kernel": "attn_fwd_kernel<",
+    "attn_decode_split_kernel": "attn_decode_split_kernel<",
+    "attn_decode_append_kernel": "attn_decode_append_kernel<",
+    "attn_bwd_dkdv_kernel": "attn_bwd_dkdv_kernel<",
+    "attn_bwd_dq_kernel": "attn_bwd_dq_kernel<",
+    "attn_fwd_fp8_kernel": "attn_fwd_fp8_kernel<",
+    "attn_fp8_quant_kernel": "attn_fp8_quant_kernel<",
+}
+
+
+def traffic_sum(keys, digest):
+    """Sum of the per-launch HBM bytes of several kernels, or None if any is missing."""
+    vals = [load_traffic(k, digest) for k in keys]
+    return None if any(v is None for v in vals) else sum(vals)
 
 
 def _counter_rows(path, counter):
@@ -158,7 +176,7 @@ def write_traffic(fetch_csv, write_csv, copy_mib, commands):
     return 0
 
 
-def time_backward(ea, pc, out, lse, stream, torch, reps=10):
+def time_backward(ea, pc, out, lse, stream, torch, digest, reps=10):
     """attn_bwd on the prefill workload, timed apart from the step.
 
     Gradients are a widening of the path (not part of the step above).  FLOPs
@@ -181,8 +199,17 @@ def time_backward(ea, pc, out, lse, stream, torch, reps=10):
     torch.cuda.synchronize()
     ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
     flops = 2.5 * prefill_flops(pc)
-    return {"kernel_ms_mean": round(ms, 4), "value": round(flops / (ms * 1e-3) / 1e12, 2),
+    tf = flops / (ms * 1e-3) / 1e12
+    n_qo = pc["B"] * pc["Nq"] * pc["Hq"] * pc["d"]
+    n_kv = pc["B"] * pc["Nk"] * pc["Hkv"] * pc["d"]
+    # read q, out, dout, k, v and lse; write dq, dk, dv (bf16)
+    alg = 2 * (3 * n_qo + 2 * n_kv) + 4 * pc["B"] * pc["Hq"] * pc["Nq"] + 2 * (n_qo + 2 * n_kv)
+    return {"kernel_ms_mean": round(ms, 4), "value": round(tf, 2),
             "unit": "TFLOP/s", "flops": flops, "flops_convention": "2.5x the forward metric FLOPs",
+            "algorithmic_bytes": alg,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_sum(["attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"], digest)},
             "workload": PREFILL}
 
 
@@ -201,7 +228,7 @@ def kvcache_bytes(case, rotary_dim):
     return kv + new + qo + table + rot
 
 
-def time_decode_kvcache(ea, W, dev, props, stream, torch, reps=20):
+def time_decode_kvcache(ea, W, dev, props, stream, torch, digest, reps=20):
     """attn_decode_kvcache (append + rotary, split, combine in one call) on the
     paged decode workload's lengths with one appended token per request and a
     rotary turn over all 128 features; timed apart from the step."""
@@ -233,15 +260,19 @@ def time_decode_kvcache(ea, W, dev, props, stream, torch, reps=20):
     torch.cuda.synchronize()
     ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
     nbytes = kvcache_bytes(kc, c["d"])
-    return {"call_ms_mean": round(ms, 4), "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"call_ms_mean": round(ms, 4), "value": round(gbs, 1), "unit": "GB/s",
             "algorithmic_bytes": nbytes, "chunk_tokens": chunk, "splits": n,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_sum(["attn_decode_append_kernel", "attn_decode_split_kernel"], digest)},
             "workload": DECODE + " with one appended token per request, rotary over all 128 features"}
 
 
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
 
 
-def time_fp8(ea, W, pc, stream, torch, reps=20):
+def time_fp8(ea, W, pc, stream, torch, digest, reps=20):
     """FP8 forward on the prefill workload, timed apart from the step: the three
     quantisation passes (Q and K turned by seeded random signs, V into the V^T
     layout) and attn_fwd_fp8, each bracketed by events.  FLOPs as the bf16
@@ -279,9 +310,14 @@ def time_fp8(ea, W, pc, stream, torch, reps=20):
     flops = prefill_flops(pc)
     tf = flops / (a_ms * 1e-3) / 1e12
     qbytes = 3 * 3 * q.numel()  # read bf16 (2 B), write codes (1 B), three tensors
+    nb = -(-pc["Nq"] // 64)
+    # read the three code tensors and their block scales, write out (bf16) and lse
+    alg = 3 * q.numel() + 3 * 4 * pc["B"] * pc["Hq"] * nb + 2 * q.numel() + 4 * pc["B"] * pc["Hq"] * pc["Nq"]
     return {"kernel_ms_mean": round(a_ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+            "algorithmic_bytes": alg,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "traffic": load_traffic("attn_fwd_fp8_kernel", digest)},
             "quantize_ms_mean": round(q_ms, 4), "quantize_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
             "end_to_end_tflops": round(flops / ((q_ms + a_ms) * 1e-3) / 1e12, 2),
             "workload": PREFILL + ", E4M3, 64-row block scales, Q and K turned by a random-sign Hadamard transform"}
@@ -435,9 +471,10 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    bwd = None if args.no_backward else time_backward(ea, pc, out, lse, stream, torch)
-    kvc = None if args.no_kvcache else time_decode_kvcache(ea, W, dev, props, stream, torch)
-    fp8 = None if args.no_fp8 else time_fp8(ea, W, pc, stream, torch)
+    digest = source_digest()
+    bwd = None if args.no_backward else time_backward(ea, pc, out, lse, stream, torch, digest)
+    kvc = None if args.no_kvcache else time_decode_kvcache(ea, W, dev, props, stream, torch, digest)
+    fp8 = None if args.no_fp8 else time_fp8(ea, W, pc, stream, torch, digest)
     pre = [e[0].elapsed_time(e[1]) for e in events]
     spl = [e[1].elapsed_time(e[2]) for e in events]
     cmb = [e[2].elapsed_time(e[3]) for e in events]
@@ -450,7 +487,6 @@ def main():
     dbytes = decode_bytes(dc)
     split_gbs = dbytes / (spl_ms * 1e-3) / 1e9
     decode_gbs = dbytes / ((spl_ms + cmb_ms) * 1e-3) / 1e9
-    digest = source_digest()
     pre_traffic = load_traffic("attn_fwd_kernel", digest)
     dec_traffic = load_traffic("attn_decode_split_kernel", digest)
 

@@ -129,33 +129,52 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t* dst, const f32x16 (&ac
 }
 
 // ---- D = rowsum(G * O) and lse in log2 units ---------------------------------
+// One wave per 16 consecutive rows of one query head: LPI lanes form one
+// row's dot product per pass, and the 16 results are gathered into lanes
+// 0..15 so that each of the two workspace arrays gets one contiguous 64-byte
+// write per wave (with one row per lane group and the heads interleaved, every
+// 4-byte result landed in a sector of its own).
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
-    constexpr int LPI = D / 8;      // lanes per (row, head)
-    constexpr int IPW = 64 / LPI;   // items per wave
+    constexpr int LPI = D / 8;        // lanes per row
+    constexpr int RPP = 64 / LPI;     // rows per pass
+    constexpr int PASSES = 16 / RPP;  // 16 rows per wave
     const int lane = threadIdx.x & 63;
-    const long item = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * IPW + lane / LPI;
-    const long n_items = (long)p.total_q * p.hq;
-    float x = 0.0f;
-    long row = 0;
-    int h = 0;
-    if (item < n_items) {
-        row = item / p.hq;
-        h = (int)(item % p.hq);
-        const long off = (row * p.hq + h) * D + (lane % LPI) * 8;
-        const u32x4 o = load16(p.out + off);
-        const u32x4 g = load16(p.dout + off);
+    const long job = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long per_head = ((long)p.total_q + 15) / 16;
+    const int h = (int)(job / per_head);
+    const long r0 = (job % per_head) * 16;
+    if (h >= p.hq) return;
+    float xs[PASSES];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x += __uint_as_float(o[j] << 16) * __uint_as_float(g[j] << 16);
-            x += __uint_as_float(o[j] & 0xffff0000u) * __uint_as_float(g[j] & 0xffff0000u);
+    for (int pass = 0; pass < PASSES; ++pass) {
+        const long row = r0 + pass * RPP + lane / LPI;
+        float x = 0.0f;
+        if (row < p.total_q) {
+            const long off = (row * p.hq + h) * D + (lane % LPI) * 8;
+            const u32x4 o = load16(p.out + off);
+            const u32x4 g = load16(p.dout + off);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x += __uint_as_float(o[j] << 16) * __uint_as_float(g[j] << 16);
+                x += __uint_as_float(o[j] & 0xffff0000u) * __uint_as_float(g[j] & 0xffff0000u);
+            }
         }
-    }
 #pragma unroll
-    for (int m = LPI / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-    if (item < n_items && lane % LPI == 0) {
+        for (int m = LPI / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+        xs[pass] = x;
+    }
+    // lane i < 16 takes row r0 + i: pass i / RPP, lane group i % RPP
+    float mine = 0.0f;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+        const float t = __shfl(xs[pass], LPI * (lane % RPP), 64);
+        if (lane / RPP == pass) mine = t;
+    }
+    const long row = r0 + lane;
+    if (lane < 16 && row < p.total_q) {
         const long w = (long)h * p.total_q + row;
-        p.dsum[w] = x;
+        p.dsum[w] = mine;
         long li;
         if (p.cu_q != nullptr) {
             li = w;  // packed lse layout [hq, total_q]
@@ -500,9 +519,8 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
     constexpr int DQ_NW = 8, DQ_WPE = 2;
     BwdParams p = p0;
     {
-        constexpr int IPB = 4 * (64 / (D / 8));  // (row, head) items per block
-        const long items = (long)p.total_q * p.hq;
-        const long grid = (items + IPB - 1) / IPB;
+        const long waves = ((long)p.total_q + 15) / 16 * p.hq;  // 16 rows of one head per wave
+        const long grid = (waves + 3) / 4;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         if (grid > 0) hipLaunchKernelGGL(attn_bwd_prep_kernel<D>, dim3((unsigned)grid), dim3(256), 0, s, p);
         const hipError_t e = hipGetLastError();
