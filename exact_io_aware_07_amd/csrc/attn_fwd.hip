@@ -404,8 +404,12 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, boo
 #ifndef ATTN_FWD128_CFG
 #define ATTN_FWD128_CFG 1, 64, 8, 2
 #endif
+// d = 64: one 32-row block per wave keeps a wave at 119 VGPRs, so four
+// workgroups of four waves share a CU (four waves per SIMD): the same rate as
+// two 64-row blocks per wave at two waves per SIMD on long sequences, and
+// twice the workgroups for short ones.
 #ifndef ATTN_FWD64_CFG
-#define ATTN_FWD64_CFG 2, 64, 4, 2
+#define ATTN_FWD64_CFG 1, 64, 4, 4
 #endif
 #ifndef ATTN_FWD256_CFG
 #define ATTN_FWD256_CFG 1, 32, 4, 1
