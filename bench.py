@@ -323,6 +323,45 @@ def time_fp8(ea, W, pc, stream, torch, digest, reps=20):
             "workload": PREFILL + ", E4M3, 64-row block scales, Q and K turned by a random-sign Hadamard transform"}
 
 
+def measure_ceilings(ea, torch, dev, stream, read_gib=4, waves=2048, iters=4096, reps=4):
+    """Measured ceilings on this GPU (include/attn_ceiling.h): a streaming read
+    of read_gib GiB, and bf16 matrix cores on random operands, two waves per
+    SIMD of four independent accumulator chains."""
+    def timed(fn):
+        fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+
+    src = torch.zeros(read_gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(ea.lib().attn_ceiling_read_sink_words(read_gib << 30), dtype=torch.int32, device=dev)
+    r_ms = timed(lambda: ea.ceiling_read(src, sink, stream=stream))
+    nbytes = src.numel()
+    del src
+    g = torch.Generator(device=dev).manual_seed(7)
+    ops = torch.randn((waves, 64, 64), generator=g, device=dev).to(torch.bfloat16).view(torch.int32)
+    sinkf = torch.empty(waves * 64, dtype=torch.float32, device=dev)
+    m_ms = timed(lambda: ea.ceiling_mfma_bf16(ops, iters, sink=sinkf, stream=stream))
+    flops = waves * iters * 32 * 32768.0
+    return {"hbm_read_gbs": round(nbytes / (r_ms * 1e-3) / 1e9, 1), "read_bytes": nbytes,
+            "mfma_bf16_random_tflops": round(flops / (m_ms * 1e-3) / 1e12, 1), "mfma_waves": waves,
+            "mfma_iters": iters,
+            "method": "each wave streams a contiguous 512 KiB of a 4 GiB buffer, 8 16-byte loads in flight per "
+                      "lane; 4 independent v_mfma_f32_32x32x16_bf16 chains per wave on random bf16 operands, 2 waves "
+                      "per SIMD (64 KiB of LDS per 4-wave workgroup keeps the grid spread over all CUs)"}
+
+
+def add_measured(roof, ceiling):
+    """Beside the published peak: the same rate against the measured ceiling."""
+    if roof is not None and ceiling:
+        roof["peak_measured"] = ceiling
+        roof["frac_measured"] = round(roof["achieved"] / ceiling, 4)
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
     import numpy as np
@@ -384,6 +423,8 @@ def main():
                     help="skip the separately timed attn_decode_kvcache leg (not part of the step)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the separately timed FP8 forward leg (not part of the step)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip measuring the HBM-read and matrix-core ceilings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for counter scaling)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -475,6 +516,7 @@ def main():
     bwd = None if args.no_backward else time_backward(ea, pc, out, lse, stream, torch, digest)
     kvc = None if args.no_kvcache else time_decode_kvcache(ea, W, dev, props, stream, torch, digest)
     fp8 = None if args.no_fp8 else time_fp8(ea, W, pc, stream, torch, digest)
+    ceil = None if args.no_ceilings else measure_ceilings(ea, torch, dev, stream)
     pre = [e[0].elapsed_time(e[1]) for e in events]
     spl = [e[1].elapsed_time(e[2]) for e in events]
     cmb = [e[2].elapsed_time(e[3]) for e in events]
@@ -528,6 +570,14 @@ def main():
                    "hip": getattr(torch.version, "hip", None)},
         "kernel_source_digest": digest,
     }
+    if ceil is not None:
+        rec["ceilings"] = ceil
+        add_measured(rec["roofline"], ceil["mfma_bf16_random_tflops"])
+        add_measured(rec["decode"]["roofline"], ceil["hbm_read_gbs"])
+        if bwd is not None:
+            add_measured(bwd["roofline"], ceil["mfma_bf16_random_tflops"])
+        if kvc is not None:
+            add_measured(kvc["roofline"], ceil["hbm_read_gbs"])
     if bwd is not None:
         rec["backward"] = bwd
     if kvc is not None:

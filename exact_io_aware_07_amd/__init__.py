@@ -57,6 +57,10 @@ _SIGNATURES = {
     "attn_fp8_codes_bytes": ([_I, _I, _I, _I, _I], ctypes.c_size_t),
     "attn_fp8_num_blocks": ([_I], _I),
     "attn_fwd_fp8": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "attn_ceiling_read_sink_words": ([ctypes.c_size_t], ctypes.c_size_t),
+    "attn_ceiling_read": ([_P, ctypes.c_size_t, _P, _P], _I),
+    "attn_ceiling_mfma_bf16": ([_P, _I, _I, _P, _P], _I),
+    "attn_ceiling_last_error": ([], ctypes.c_char_p),
     "attn_decode_num_splits": ([_I, _I], _I),
     "attn_decode_default_chunk": ([_I, _I, _I, _I], _I),
     "attn_decode_workspace_bytes": ([_I, _I, _I, _I], ctypes.c_size_t),
@@ -543,6 +547,39 @@ def attn_fp8_forward(q, k, v, *, causal, softmax_scale, signs=None, stream=None)
     vc, vs = attn_fp8_quantize(v, layout="vt", stream=stream)
     return attn_fwd_fp8(qc, kc, vc, qs, ks, vs, causal=causal, softmax_scale=softmax_scale,
                         incoherent=signs is not None, stream=stream)
+
+
+def ceiling_read(src, sink=None, stream=None):
+    """Measurement helper: stream-read every byte of the GPU tensor `src`
+    (contiguous, size a multiple of 16 bytes).  Returns the sink tensor."""
+    dev = src.device
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if sink is None:
+        sink = torch.empty(lib().attn_ceiling_read_sink_words(src.numel() * src.element_size()), dtype=torch.int32,
+                           device=dev)
+    with torch.cuda.device(dev):
+        st = lib().attn_ceiling_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream, dev))
+    if st != 0:
+        raise AttnError(st, lib().attn_ceiling_last_error().decode())
+    return sink
+
+
+def ceiling_mfma_bf16(operands, iters, sink=None, stream=None):
+    """Measurement helper: bf16 matrix-core loop on `operands` (int32 GPU tensor
+    [waves, 64, 32] of random bf16 pairs).  Returns the sink tensor [waves * 64]."""
+    dev = operands.device
+    _need(operands, "operands", torch.int32, dev)
+    waves = operands.shape[0]
+    if tuple(operands.shape) != (waves, 64, 32):
+        raise ValueError("operands must be [waves, 64, 32]")
+    if sink is None:
+        sink = torch.empty(waves * 64, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = lib().attn_ceiling_mfma_bf16(_ptr(operands), waves, int(iters), _ptr(sink), _stream(stream, dev))
+    if st != 0:
+        raise AttnError(st, lib().attn_ceiling_last_error().decode())
+    return sink
 
 
 def attn_check_cu_seqlens(cu_seqlens, total, max_seqlen):

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fp8.hip", "attn_api.hip"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fp8.hip", "attn_ceiling.hip", "attn_api.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for device code on purpose.

@@ -22,9 +22,13 @@ NULL = None
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "attn.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -290,3 +294,23 @@ ODD = ctypes.c_void_p(0x10000 + 2)   # 2-byte aligned: fine for no tensor
 def test_misaligned_pointers_rejected(call, kw):
     """Misaligned tensors are refused before any launch (ATTN_ERR_UNSUPPORTED)."""
     assert call(**kw) == 3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(src=NULL), 1), (dict(sink=NULL), 1), (dict(nbytes=0), 2), (dict(nbytes=100), 2),
+    (dict(src=ctypes.c_void_p(0x10000 + 8)), 3),
+])
+def test_ceiling_read_rejects(kw, code):
+    a = dict(src=FAKE, nbytes=1 << 20, sink=OUT)
+    a.update(kw)
+    assert ea.lib().attn_ceiling_read(a["src"], a["nbytes"], a["sink"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ops=NULL), 1), (dict(sink=NULL), 1), (dict(waves=6), 2), (dict(waves=0), 2), (dict(iters=0), 2),
+    (dict(ops=ctypes.c_void_p(0x10000 + 4)), 3),
+])
+def test_ceiling_mfma_rejects(kw, code):
+    a = dict(ops=FAKE, waves=8, iters=10, sink=OUT)
+    a.update(kw)
+    assert ea.lib().attn_ceiling_mfma_bf16(a["ops"], a["waves"], a["iters"], a["sink"], None) == code
