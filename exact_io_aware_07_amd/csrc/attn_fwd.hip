@@ -40,7 +40,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 void attn_fwd_kernel(FwdParams p) {
     static_assert(!PAGED || VARLEN, "paged prefill packs its queries");
     static_assert(kFwdPage % BC == 0, "key tiles must not straddle pages");
-    constexpr int NT = NW * 64;
     constexpr int ROWS_W = 32 * QB;
     constexpr int BR = NW * ROWS_W;
     constexpr int KB = BC / 32;  // 32-key blocks per tile

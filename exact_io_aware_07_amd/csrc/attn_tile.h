@@ -236,13 +236,21 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
 // writes: it would otherwise drain every outstanding load before LDS reads it
 // cannot prove unrelated.  Every consumer waits explicitly (wait_vmem*)
 // before reading a stage and synchronises as needed.
+// M0 is saved and restored around the load (M0 is a reserved register that a
+// clobber list does not protect; the load takes its value at issue), and one
+// wait state separates the M0 write from the load, as GFX9-family parts
+// require between an SALU write of M0 and an LDS-DMA instruction.
 __device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds_base, uint32_t voff) {
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
-        :
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
         : "s"(lds_base), "v"(voff), "s"(rsrc)
-        : "memory", "m0");
+        : "memory");
 }
 
 // Swizzle for V rows read by ds_read_b64_tr_b16: one instruction touches 8
