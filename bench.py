@@ -347,12 +347,17 @@ def measure_ceilings(ea, torch, dev, stream, read_gib=4, waves=2048, iters=4096,
     sinkf = torch.empty(waves * 64, dtype=torch.float32, device=dev)
     m_ms = timed(lambda: ea.ceiling_mfma_bf16(ops, iters, sink=sinkf, stream=stream))
     flops = waves * iters * 32 * 32768.0
+    ops8 = torch.randn((waves, 64, 256), generator=g, device=dev).to(torch.float8_e4m3fn).view(torch.int32)
+    f_ms = timed(lambda: ea.ceiling_mfma_fp8(ops8, iters, sink=sinkf, stream=stream))
+    flops8 = waves * iters * 32 * 131072.0
     return {"hbm_read_gbs": round(nbytes / (r_ms * 1e-3) / 1e9, 1), "read_bytes": nbytes,
-            "mfma_bf16_random_tflops": round(flops / (m_ms * 1e-3) / 1e12, 1), "mfma_waves": waves,
+            "mfma_bf16_random_tflops": round(flops / (m_ms * 1e-3) / 1e12, 1),
+            "mfma_fp8_random_tflops": round(flops8 / (f_ms * 1e-3) / 1e12, 1), "mfma_waves": waves,
             "mfma_iters": iters,
             "method": "each wave streams a contiguous 512 KiB of a 4 GiB buffer, 8 16-byte loads in flight per "
-                      "lane; 4 independent v_mfma_f32_32x32x16_bf16 chains per wave on random bf16 operands, 2 waves "
-                      "per SIMD (64 KiB of LDS per 4-wave workgroup keeps the grid spread over all CUs)"}
+                      "lane; 4 independent v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x64_f8f6f4) chains per wave on "
+                      "N(0,1) bf16 (E4M3) operands, 2 waves per SIMD (64 KiB of LDS per 4-wave workgroup keeps the "
+                      "grid spread over all CUs)"}
 
 
 def add_measured(roof, ceiling):
@@ -578,6 +583,8 @@ def main():
             add_measured(bwd["roofline"], ceil["mfma_bf16_random_tflops"])
         if kvc is not None:
             add_measured(kvc["roofline"], ceil["hbm_read_gbs"])
+        if fp8 is not None:
+            add_measured(fp8["roofline"], ceil["mfma_fp8_random_tflops"])
     if bwd is not None:
         rec["backward"] = bwd
     if kvc is not None:

@@ -60,6 +60,7 @@ _SIGNATURES = {
     "attn_ceiling_read_sink_words": ([ctypes.c_size_t], ctypes.c_size_t),
     "attn_ceiling_read": ([_P, ctypes.c_size_t, _P, _P], _I),
     "attn_ceiling_mfma_bf16": ([_P, _I, _I, _P, _P], _I),
+    "attn_ceiling_mfma_fp8": ([_P, _I, _I, _P, _P], _I),
     "attn_ceiling_last_error": ([], ctypes.c_char_p),
     "attn_decode_num_splits": ([_I, _I], _I),
     "attn_decode_default_chunk": ([_I, _I, _I, _I], _I),
@@ -565,21 +566,32 @@ def ceiling_read(src, sink=None, stream=None):
     return sink
 
 
-def ceiling_mfma_bf16(operands, iters, sink=None, stream=None):
-    """Measurement helper: bf16 matrix-core loop on `operands` (int32 GPU tensor
-    [waves, 64, 32] of random bf16 pairs).  Returns the sink tensor [waves * 64]."""
+def _ceiling_mfma(fn, words, operands, iters, sink, stream):
     dev = operands.device
     _need(operands, "operands", torch.int32, dev)
     waves = operands.shape[0]
-    if tuple(operands.shape) != (waves, 64, 32):
-        raise ValueError("operands must be [waves, 64, 32]")
+    if tuple(operands.shape) != (waves, 64, words):
+        raise ValueError(f"operands must be [waves, 64, {words}]")
     if sink is None:
         sink = torch.empty(waves * 64, dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
-        st = lib().attn_ceiling_mfma_bf16(_ptr(operands), waves, int(iters), _ptr(sink), _stream(stream, dev))
+        st = fn(_ptr(operands), waves, int(iters), _ptr(sink), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, lib().attn_ceiling_last_error().decode())
     return sink
+
+
+def ceiling_mfma_bf16(operands, iters, sink=None, stream=None):
+    """Measurement helper: bf16 matrix-core loop on `operands` (int32 GPU tensor
+    [waves, 64, 32] of random bf16 pairs).  Returns the sink tensor [waves * 64]."""
+    return _ceiling_mfma(lib().attn_ceiling_mfma_bf16, 32, operands, iters, sink, stream)
+
+
+def ceiling_mfma_fp8(operands, iters, sink=None, stream=None):
+    """Measurement helper: E4M3 matrix-core loop on `operands` (int32 GPU tensor
+    [waves, 64, 64] of finite E4M3 codes, four per word).  Returns the sink
+    tensor [waves * 64]."""
+    return _ceiling_mfma(lib().attn_ceiling_mfma_fp8, 64, operands, iters, sink, stream)
 
 
 def attn_check_cu_seqlens(cu_seqlens, total, max_seqlen):

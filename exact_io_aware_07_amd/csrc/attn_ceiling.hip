@@ -1,6 +1,6 @@
-// Measured ceilings of the two resources the attention kernels are bound by
-// (gfx950): streaming HBM reads and bf16 matrix-core throughput on random
-// operands.  Not part of the method: the benchmark reports each kernel's
+// Measured ceilings of the resources the attention kernels are bound by
+// (gfx950): streaming HBM reads, and bf16 and E4M3 matrix-core throughput on
+// random operands.  Not part of the method: the benchmark reports each kernel's
 // rate against these as well as against the published peaks ("Deep Dive -
 // FlashAttention", "Benchmark the path you will ship", and "FlashAttention-3
 // and PagedAttention: IO-Aware Attention Kernels (2026)", "Runnable Example:
@@ -40,21 +40,51 @@ __global__ __launch_bounds__(64) void ceiling_read_kernel(const attn::u32x4* src
     if (lane == 0) sink[blockIdx.x] = x;
 }
 
-// Four accumulator chains of v_mfma_f32_32x32x16_bf16 per wave, operands
-// cycled among eight fragments of random bf16 values per lane (values that
-// toggle the multipliers as real data does; constant operands run at a
-// higher clock), 32 products per iteration.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One 32x32 matrix-core product: bf16 (v_mfma_f32_32x32x16_bf16, 16 bytes of
+// operand per lane) or E4M3 (v_mfma_f32_32x32x64_f8f6f4 with format 0 for both
+// operands, 32 bytes per lane).
+template <bool FP8>
+struct CeilOp;
+template <>
+struct CeilOp<false> {
+    using Frag = attn::u32x4;
+    static constexpr int WORDS = 4;
+    static __device__ __forceinline__ Frag load(const uint32_t* w) { return Frag{w[0], w[1], w[2], w[3]}; }
+    static __device__ __forceinline__ attn::f32x16 mma(const Frag& a, const Frag& b, const attn::f32x16& c) {
+        return attn::mfma32(a, b, c);
+    }
+};
+template <>
+struct CeilOp<true> {
+    using Frag = i32x8;
+    static constexpr int WORDS = 8;
+    static __device__ __forceinline__ Frag load(const uint32_t* w) {
+        return Frag{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    }
+    static __device__ __forceinline__ attn::f32x16 mma(const Frag& a, const Frag& b, const attn::f32x16& c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+    }
+};
+
+// Four accumulator chains of 32x32 products per wave, operands cycled among
+// eight fragments of random values per lane (values that toggle the
+// multipliers as real data does; constant operands run at a higher clock),
+// 32 products per iteration.
+template <bool FP8>
 __global__ __launch_bounds__(256) void ceiling_mfma_kernel(const uint32_t* ops, int iters, float* sink) {
+    using Op = CeilOp<FP8>;
     // 64 KiB of LDS per workgroup (of 160 KiB per CU) leaves room for two
     // workgroups per CU, so the grid spreads two waves onto every SIMD instead
     // of piling more onto some compute units and leaving others idle.
     __shared__ float spread[16384];
     const int lane = threadIdx.x & 63;
     const long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const uint32_t* my = ops + (w * 64 + lane) * 32;
-    attn::u32x4 f[8];
+    const uint32_t* my = ops + (w * 64 + lane) * (8 * Op::WORDS);
+    typename Op::Frag f[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = attn::u32x4{my[4 * i], my[4 * i + 1], my[4 * i + 2], my[4 * i + 3]};
+    for (int i = 0; i < 8; ++i) f[i] = Op::load(my + Op::WORDS * i);
     attn::f32x16 acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -64,7 +94,7 @@ __global__ __launch_bounds__(256) void ceiling_mfma_kernel(const uint32_t* ops, 
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = attn::mfma32(f[(j + c) & 7], f[(j + 2 * c + 1) & 7], acc[c]);
+            for (int c = 0; c < 4; ++c) acc[c] = Op::mma(f[(j + c) & 7], f[(j + 2 * c + 1) & 7], acc[c]);
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -91,6 +121,19 @@ attn_status_t launched(const char* what) {
     return ATTN_OK;
 }
 
+template <bool FP8>
+attn_status_t ceiling_mfma(const uint32_t* operands, int waves, int iters, float* sink, void* stream,
+                           const char* what) {
+    if (!operands || !sink) return fail(ATTN_ERR_NULL, "operands and sink must be non-NULL");
+    if (((uintptr_t)operands & 15u) || ((uintptr_t)sink & 3u))
+        return fail(ATTN_ERR_UNSUPPORTED, "misaligned pointer");
+    if (waves < 4 || waves % 4 || iters < 1)
+        return fail(ATTN_ERR_SHAPE, "waves must be a positive multiple of 4 and iters >= 1");
+    hipLaunchKernelGGL(ceiling_mfma_kernel<FP8>, dim3(waves / 4), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       operands, iters, sink);
+    return launched(what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,14 +152,11 @@ attn_status_t attn_ceiling_read(const void* src, size_t bytes, uint32_t* sink, v
 }
 
 attn_status_t attn_ceiling_mfma_bf16(const uint32_t* operands, int waves, int iters, float* sink, void* stream) {
-    if (!operands || !sink) return fail(ATTN_ERR_NULL, "operands and sink must be non-NULL");
-    if (((uintptr_t)operands & 15u) || ((uintptr_t)sink & 3u))
-        return fail(ATTN_ERR_UNSUPPORTED, "misaligned pointer");
-    if (waves < 4 || waves % 4 || iters < 1)
-        return fail(ATTN_ERR_SHAPE, "waves must be a positive multiple of 4 and iters >= 1");
-    hipLaunchKernelGGL(ceiling_mfma_kernel, dim3(waves / 4), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       operands, iters, sink);
-    return launched("attn_ceiling_mfma_bf16 launch");
+    return ceiling_mfma<false>(operands, waves, iters, sink, stream, "attn_ceiling_mfma_bf16 launch");
+}
+
+attn_status_t attn_ceiling_mfma_fp8(const uint32_t* operands, int waves, int iters, float* sink, void* stream) {
+    return ceiling_mfma<true>(operands, waves, iters, sink, stream, "attn_ceiling_mfma_fp8 launch");
 }
 
 const char* attn_ceiling_last_error(void) { return g_err; }

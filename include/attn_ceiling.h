@@ -1,7 +1,7 @@
 /*
  * Measured ceilings for the attention kernels' rooflines (libattn.so).
  *
- * Not part of the attention method: two kernels that measure, on the machine
+ * Not part of the attention method: kernels that measure, on the machine
  * at hand, the rates the attention kernels are bound by, so that each kernel
  * can be reported against the measured ceiling as well as the published peak
  * ("Deep Dive - FlashAttention", "Benchmark the path you will ship";
@@ -46,6 +46,14 @@ attn_status_t attn_ceiling_read(const void* src, size_t bytes, uint32_t* sink, v
  * Rate = waves * iters * 32 * 32768 / kernel time.
  */
 attn_status_t attn_ceiling_mfma_bf16(const uint32_t* operands, int waves, int iters, float* sink, void* stream);
+
+/*
+ * As attn_ceiling_mfma_bf16 for E4M3 operands: v_mfma_f32_32x32x64_f8f6f4
+ * products (131072 FLOP each), 8 fragments of 32 E4M3 codes per lane from
+ * `operands`: uint32 [waves, 64 lanes, 64] (finite codes; no NaN byte 0x7F or
+ * 0xFF).  Rate = waves * iters * 32 * 131072 / kernel time.
+ */
+attn_status_t attn_ceiling_mfma_fp8(const uint32_t* operands, int waves, int iters, float* sink, void* stream);
 
 /* The calling thread's message for its last failing ceiling call. */
 const char* attn_ceiling_last_error(void);

@@ -310,7 +310,8 @@ def test_ceiling_read_rejects(kw, code):
     (dict(ops=NULL), 1), (dict(sink=NULL), 1), (dict(waves=6), 2), (dict(waves=0), 2), (dict(iters=0), 2),
     (dict(ops=ctypes.c_void_p(0x10000 + 4)), 3),
 ])
-def test_ceiling_mfma_rejects(kw, code):
+@pytest.mark.parametrize("fn", ["attn_ceiling_mfma_bf16", "attn_ceiling_mfma_fp8"])
+def test_ceiling_mfma_rejects(fn, kw, code):
     a = dict(ops=FAKE, waves=8, iters=10, sink=OUT)
     a.update(kw)
-    assert ea.lib().attn_ceiling_mfma_bf16(a["ops"], a["waves"], a["iters"], a["sink"], None) == code
+    assert getattr(ea.lib(), fn)(a["ops"], a["waves"], a["iters"], a["sink"], None) == code

@@ -1,9 +1,10 @@
-"""The two measurement kernels of include/attn_ceiling.h compute what they claim (needs an MI355X).
+"""The measurement kernels of include/attn_ceiling.h compute what they claim (needs an MI355X).
 
 The read kernel's sink words are the XOR of each 512 KiB chunk, checked with
-numpy on a buffer with a ragged last chunk.  The matrix-core kernel, given
+numpy on a buffer with a ragged last chunk.  The matrix-core kernels, given
 fragments that each hold one small integer, must return the exact sum that
-its four chains of fragment pairs imply (every product entry is 16 * a * b).
+their four chains of fragment pairs imply (every product entry is K * a * b,
+K = 16 for bf16 and 64 for E4M3).
 """
 import numpy as np
 import pytest
@@ -28,13 +29,22 @@ def test_read_sink_is_xor_of_each_chunk():
     assert got.tolist() == [int(x) for x in want]
 
 
-def test_mfma_sink_matches_the_fragment_schedule():
-    waves, iters = 8, 3
-    vals = np.arange(1, 9, dtype=np.float64)  # fragment i holds the value i + 1 in all 8 slots
-    frag = torch.tensor(vals, dtype=torch.bfloat16).view(1, 1, 8, 1).expand(waves, 64, 8, 8).contiguous()
-    ops = frag.view(waves, 64, 64).view(torch.int32).to(DEV)
-    sink = ea.ceiling_mfma_bf16(ops, iters)
-    torch.cuda.synchronize()
-    per_lane = sum(16 * iters * sum(16 * vals[(j + c) % 8] * vals[(j + 2 * c + 1) % 8] for j in range(8))
+def expected_sink(vals, iters, k):
+    per_lane = sum(16 * iters * sum(k * vals[(j + c) % 8] * vals[(j + 2 * c + 1) % 8] for j in range(8))
                    for c in range(4))
-    assert torch.equal(sink.cpu(), torch.full((waves * 64,), 2 * per_lane, dtype=torch.float32))
+    return 2 * per_lane  # each lane adds the sum of the lane 64 threads on
+
+
+# (element type, K of one product, values per lane per fragment, binding)
+@pytest.mark.parametrize("dtype,k,per_frag,fn", [(torch.bfloat16, 16, 8, "ceiling_mfma_bf16"),
+                                                 (torch.float8_e4m3fn, 64, 32, "ceiling_mfma_fp8")])
+def test_mfma_sink_matches_the_fragment_schedule(dtype, k, per_frag, fn):
+    waves, iters = 8, 3
+    vals = np.arange(1, 9, dtype=np.float64)  # fragment i holds the value i + 1 in every slot
+    frag = torch.tensor(vals, dtype=torch.float32).to(dtype).view(1, 1, 8, 1).expand(waves, 64, 8, per_frag)
+    ops = frag.contiguous().view(waves, 64, 8 * per_frag).view(torch.int32).to(DEV)
+    sink = getattr(ea, fn)(ops, iters)
+    torch.cuda.synchronize()
+    want = expected_sink(vals, iters, k)
+    assert want < 2**24  # every partial sum is an exact fp32 integer
+    assert torch.equal(sink.cpu(), torch.full((waves * 64,), want, dtype=torch.float32))
