@@ -338,6 +338,7 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     for (int i = lane; i < p.nbk; i += 64) svmax = fmaxf(svmax, vs_row[i]);
     svmax = wave_max_f(svmax);
     const float vref = svmax > 0.0f ? svmax : 1.0f;
+    const float log2_svmax = svmax > 0.0f ? __log2f(svmax) : 0.0f;
     const float c2q = p.scale * kLog2e * s_q;
 
     f32x16 oacc[4];
@@ -347,14 +348,27 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     float m_run = -INFINITY, l_part = 0.0f;
 
-    if (t_end > 0) issue_tile(0, lds_addr(stage0));
+    // The K and V scales of a tile are loaded one step ahead, with the tile's
+    // own loads, so that the end-of-step wait covers them: a load waited for
+    // inside a step would also wait for the next tile's loads issued before it.
+    float ks_cur = 0.0f, vs_cur = 0.0f;
+    if (t_end > 0) {
+        issue_tile(0, lds_addr(stage0));
+        ks_cur = ks_row[0];
+        vs_cur = vs_row[0];
+    }
     wait_vmem();
     __syncthreads();
 
     auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
         const char* ks = cur;
         const char* vs = cur + K_BYTES;
-        if (t + 1 < t_end) issue_tile(t + 1, lds_addr(nxt));
+        float ks_nxt = 0.0f, vs_nxt = 0.0f;
+        if (t + 1 < t_end) {
+            issue_tile(t + 1, lds_addr(nxt));
+            ks_nxt = ks_row[t + 1];
+            vs_nxt = vs_row[t + 1];
+        }
         const int k0 = t * BC;
         const bool active = wave_rows && k0 <= w_hi_max;
         if (active) {
@@ -376,7 +390,7 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
                     sacc[kb] = mfma_fp8(a, qf[s], sacc[kb]);
                 }
             // scores of the turned, dequantised operands in log2 units: S * c2t
-            const float c2t = fmaxf(c2q * ks_row[t], 1.17549435e-38f);
+            const float c2t = fmaxf(c2q * ks_cur, 1.17549435e-38f);
             if (k0 + BC - 1 > w_hi_min || k0 + BC > Nk) {
                 const int hi = hi_of(row);
 #pragma unroll
@@ -402,8 +416,8 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
             }
             if (raise) m_run = mx;
             // V tile scale folded into P: P' = p * 64 * s_v(t) / max s_v
-            const float sv = vs_row[t];
-            const float lg = kFp8PScale + ((sv > 0.0f && svmax > 0.0f) ? __log2f(sv) - __log2f(svmax) : 0.0f);
+            const float sv = vs_cur;
+            const float lg = kFp8PScale + ((sv > 0.0f && svmax > 0.0f) ? __log2f(sv) - log2_svmax : 0.0f);
             const float inv_g = exp2f(-lg);
             const float sh = (m_run == -INFINITY) ? 0.0f : m_run - lg;
             float rs = 0.0f;
@@ -436,6 +450,8 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
         }
         wait_vmem();
         __syncthreads();
+        ks_cur = ks_nxt;
+        vs_cur = vs_nxt;
     };
     for (int t = 0; t < t_end; t += 2) {
         step(t, stage0, stage1);
