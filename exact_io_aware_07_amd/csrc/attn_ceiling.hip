@@ -18,7 +18,8 @@ constexpr int kChunkBytes = 512 * 1024;  // contiguous bytes streamed by one wav
 constexpr int kUnroll = 8;               // 16-byte loads in flight per lane
 
 // One wave per 64-thread workgroup streams its own contiguous 512 KiB chunk,
-// eight 16-byte loads in flight per lane, and folds what it read into one
+// eight 16-byte non-temporal loads in flight per lane (the policy the decode
+// kernel uses for its read-once K/V stream), and folds what it read into one
 // word (so the loads cannot be dropped).
 __global__ __launch_bounds__(64) void ceiling_read_kernel(const attn::u32x4* src, long n16, uint32_t* sink) {
     const int lane = threadIdx.x;
@@ -29,11 +30,11 @@ __global__ __launch_bounds__(64) void ceiling_read_kernel(const attn::u32x4* src
     for (; i + 64 * (kUnroll - 1) < end; i += 64 * kUnroll) {
         attn::u32x4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + 64 * u];
+        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(&src[i + 64 * u]);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
     }
-    for (; i < end; i += 64) acc ^= src[i];
+    for (; i < end; i += 64) acc ^= __builtin_nontemporal_load(&src[i]);
     uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x ^= (uint32_t)__shfl_xor((int)x, m, 64);

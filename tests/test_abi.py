@@ -253,6 +253,13 @@ def test_host_helpers():
     for args in [(64, 8, 32768, 256), (1, 1, 100, 256), (2, 32, 1 << 20, 304)]:
         c = ea.attn_decode_default_chunk(*args)
         assert c >= 256 and c % 256 == 0
+    # 32 split waves per compute unit, chunks lengthened toward 2048 tokens
+    # while 8 waves per compute unit remain; small batches keep short chunks.
+    assert ea.attn_decode_default_chunk(64, 8, 32768, 256) == 2048
+    assert ea.attn_decode_default_chunk(64, 8, 8192, 256) == 2048
+    assert ea.attn_decode_default_chunk(64, 8, 2048, 256) == 512
+    assert ea.attn_decode_default_chunk(1, 8, 32768, 256) == 256
+    assert ea.attn_decode_default_chunk(1, 1, 1 << 20, 256) == 512
     assert ea.attn_decode_workspace_bytes(64, 32, 128, 16) == 16 * 64 * 32 * 129 * 4
 
 
