@@ -15,7 +15,9 @@
 //                         the tile's K and V stay in registers while the
 //                         query tiles of every query head of the group stream
 //                         through LDS; dK and dV accumulate in registers, so
-//                         no atomics and a fixed summation order;
+//                         no atomics and a fixed summation order (d = 64);
+//   attn_bwd_dkdv_pair_kernel  the same with each 32-key group split over two
+//                         waves, one for P and dV, one for dS and dK (d = 128);
 //   attn_bwd_dq_kernel    one workgroup per (query tile, query head,
 //                         sequence), shaped like the forward: K/V tiles stream
 //                         through LDS and dQ accumulates in registers.
@@ -366,6 +368,205 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
+// dK, dV with the work of each 32-key group split over a pair of waves, so
+// that two waves per SIMD fit the registers (one wave holding both dK and dV
+// and K and V needs about 360): wave w (w < NP) forms S = Q K^T, the mask
+// and P = exp(S - lse), hands P to wave w + NP through LDS and accumulates
+// dV^T += G^T P; wave w + NP forms dP = G V^T, dS = P o (dP - D) and
+// accumulates dK^T += Q^T dS.  The two waves of a pair share a SIMD (waves w
+// and w + 4 of an 8-wave workgroup), so each one's vector work runs beside
+// the other's matrix products.  Same arithmetic and the same order of
+// accumulation per register as attn_bwd_dkdv_kernel.
+template <int D, int NP, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_pair_kernel(BwdParams p) {
+    constexpr int NW = 2 * NP;
+    constexpr int QBLK = 64;       // query rows per LDS stage
+    constexpr int KT = 32 * NP;    // keys per workgroup
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    using Tile = BwdTile<D, QBLK, NW>;
+    constexpr uint32_t STAGE = Tile::BYTES + 2 * QBLK * 4;  // Q, G, then lse2 and D of the block
+    constexpr uint32_t XBYTES = 2 * 16 * 64 * 4;            // P of one pair: 2 blocks x 16 floats x 64 lanes
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char xchg[NP * XBYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool side_p = wave < NP;  // P side (S, mask, exp, dV) or dS side (dP, dS, dK)
+    const int pair = side_p ? wave : wave - NP;
+    const int l32 = lane & 31;
+
+    const int BH = p.batch * p.hkv;
+    const int kt = blockIdx.x / BH;
+    const int b = (blockIdx.x % BH) / p.hkv;
+    const int kvh = blockIdx.x % p.hkv;
+    int q_off, k_off, Nq, Nk;
+    if constexpr (VARLEN) {
+        q_off = p.cu_q[b];
+        Nq = p.cu_q[b + 1] - q_off;
+        k_off = p.cu_k[b];
+        Nk = p.cu_k[b + 1] - k_off;
+        Nq = Nq < 0 ? 0 : Nq;
+        Nk = Nk < 0 ? 0 : Nk;
+    } else {
+        q_off = b * p.max_q;
+        Nq = p.max_q;
+        k_off = b * p.max_k;
+        Nk = p.max_k;
+    }
+    const int j0 = kt * KT;
+    if (j0 >= Nk) return;
+    const int kw0 = j0 + 32 * pair;
+    const int key = kw0 + l32;
+    const int shift = Nk - Nq;  // causal: row i sees keys j <= i + shift
+
+    // K (P side) or V (dS side) fragments of the pair's 32 keys, resident.
+    u32x4 kv[KS];
+    {
+        const long off = ((long)(k_off + key) * p.hkv + kvh) * D;
+        const uint16_t* src = side_p ? p.k : p.v;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (key < Nk) z = load16(src + off + (2 * s + (lane >> 5)) * 8);
+            kv[s] = z;
+        }
+    }
+    f32x16 acc[DB];  // dV^T (P side) or dK^T (dS side)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+    const int g = p.hq / p.hkv;
+    int qb_lo = 0;
+    if constexpr (CAUSAL) {
+        const int i_min = j0 - shift;
+        qb_lo = i_min > 0 ? i_min / QBLK : 0;
+    }
+    const int qb_hi = (Nq + QBLK - 1) / QBLK;
+    const int n_qb = qb_hi > qb_lo ? qb_hi - qb_lo : 0;
+    const int n_it = g * n_qb;
+    const uint32_t stride_q = (uint32_t)p.hq * D * 2;
+    const float c2 = p.scale * kLog2e;
+    // This pair's P: float index ((rb * 4 + q) * 64 + lane) * 4 + j holds register 4 q + j of block rb.
+    f32x4* const xp = reinterpret_cast<f32x4*>(xchg + pair * XBYTES);
+
+    auto issue = [&](int it, char* st) __attribute__((always_inline)) {
+        const int h = kvh * g + it / n_qb;
+        const int qs = (qb_lo + it % n_qb) * QBLK;
+        const long off = ((long)(q_off + qs) * p.hq + h) * D;
+        Tile::issue(p.q + off, p.dout + off, stride_q, Nq - qs, lds_addr(st), wave, lane);
+        if (wave == 0) {
+            const int nv = Nq - qs < QBLK ? Nq - qs : QBLK;
+            const long w = (long)h * p.total_q + q_off + qs;
+            const uint32_t voff = (uint32_t)(lane & 15) * 16;
+            if (lane < 16) dma16(rsrc_words(p.lse2 + w, (uint32_t)nv * 4), lds_addr(st) + Tile::BYTES, voff);
+            if (lane >= 16 && lane < 32)
+                dma16(rsrc_words(p.dsum + w, (uint32_t)nv * 4), lds_addr(st) + Tile::BYTES, voff);
+        }
+    };
+
+    if (n_it > 0) issue(0, stage0);
+    wait_vmem();
+    __syncthreads();
+
+    auto step = [&](int it, char* cur, char* nxt) __attribute__((always_inline)) {
+        if (it + 1 < n_it) issue(it + 1, nxt);
+        const int qs = (qb_lo + it % n_qb) * QBLK;
+        const bool active = kw0 < Nk && (!CAUSAL || qs + QBLK - 1 >= kw0 - shift);
+        const char* qt = cur;
+        const char* gt = cur + Tile::A_BYTES;
+        const float* lv = reinterpret_cast<const float*>(cur + Tile::BYTES);
+        f32x16 sacc[2];
+        u32x4 pw[2][2];  // packed P (P side) or dS (dS side) B operands
+        // ---- phase 1: S and P (P side) / dP (dS side) ----------------------
+        if (active) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    sacc[rb] = mfma32(rd_row<D>(side_p ? qt : gt, rb, s, lane), kv[s], sacc[rb]);
+            }
+            if (side_p) {
+                const bool need_mask = (qs + QBLK > Nq) || (kw0 + 31 >= Nk) ||
+                                       (CAUSAL && kw0 + 31 > qs + shift);
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    if (need_mask) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int i = qs + 32 * rb + acc_row(r, lane);
+                            const bool keep = i < Nq && key < Nk && (!CAUSAL || key <= i + shift);
+                            if (!keep) sacc[rb][r] = -INFINITY;
+                        }
+                    }
+                    // lse2 of the 16 rows this lane holds: rows 32 rb + 8 q4 + 4 (l / 32) .. + 3.
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 l2 = *reinterpret_cast<const f32x4*>(lv + 32 * rb + 8 * q4 + 4 * (lane >> 5));
+                        f32x4 pr;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            pr[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * q4 + j], c2, -l2[j]));
+                            sacc[rb][4 * q4 + j] = pr[j];
+                        }
+                        xp[(rb * 4 + q4) * 64 + lane] = pr;
+                    }
+                    pack_acc(sacc[rb], pw[rb]);
+                }
+            }
+        }
+        // P is in LDS for the dS side.
+        __syncthreads();
+        // ---- phase 2: dV (P side) / dS and dK (dS side) --------------------
+        if (active) {
+            if (!side_p) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 pr = xp[(rb * 4 + q4) * 64 + lane];
+                        const f32x4 dd = *reinterpret_cast<const f32x4*>(lv + QBLK + 32 * rb + 8 * q4 + 4 * (lane >> 5));
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            sacc[rb][4 * q4 + j] = pr[j] * (sacc[rb][4 * q4 + j] - dd[j]);
+                    }
+                    pack_acc(sacc[rb], pw[rb]);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        acc[db] = mfma32(rd_tr<D>(side_p ? gt : qt, db, rb, c, lane), pw[rb][c], acc[db]);
+        }
+        // The next tile has landed, and the dS side has read P before the P
+        // side overwrites it.
+        wait_vmem();
+        __syncthreads();
+    };
+    for (int it = 0; it < n_it; it += 2) {
+        step(it, stage0, stage1);
+        if (it + 1 < n_it) step(it + 1, stage1, stage0);
+    }
+
+    if (key < Nk) {
+        const long off = ((long)(k_off + key) * p.hkv + kvh) * D;
+        if (side_p)
+            store_rows_bf16<DB>(p.dv + off, acc, 1.0f, lane);
+        else
+            store_rows_bf16<DB>(p.dk + off, acc, p.scale, lane);
+    }
+}
+
 // ---- dQ ------------------------------------------------------------------------
 // Shaped like the forward: wave w owns query rows q0 + 32 w .. + 31 (lane l:
 // row l % 32).  Per 64-key tile: S^T = K Q^T and dP^T = V G^T, P^T, dS^T,
@@ -515,7 +716,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 // ---- launchers -------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
-    constexpr int DKDV_NW = 4, DKDV_WPE = D <= 64 ? 2 : 1;
+    constexpr int DKDV_NW = 4, DKDV_WPE = 2;  // d = 64: two 4-wave workgroups per CU
     constexpr int DQ_NW = 8, DQ_WPE = 2;
     BwdParams p = p0;
     {
@@ -531,9 +732,16 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
         p.n_tiles = (p.max_k + KT - 1) / KT;
         const long grid = (long)p.n_tiles * p.batch * p.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-        if (grid > 0)
-            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DKDV_NW, DKDV_WPE, CAUSAL, VARLEN>), dim3((unsigned)grid),
-                               dim3(DKDV_NW * 64), 0, s, p);
+        if (grid > 0) {
+            // d = 128: one wave per SIMD would hold both accumulators, so the
+            // work of each 32-key group is split over a pair of waves.
+            if constexpr (D == 128)
+                hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, DKDV_NW, CAUSAL, VARLEN>), dim3((unsigned)grid),
+                                   dim3(2 * DKDV_NW * 64), 0, s, p);
+            else
+                hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DKDV_NW, DKDV_WPE, CAUSAL, VARLEN>),
+                                   dim3((unsigned)grid), dim3(DKDV_NW * 64), 0, s, p);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
