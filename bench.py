@@ -100,7 +100,7 @@ TRAFFIC_KERNELS = {
     "attn_fwd_kernel": "attn_fwd_kernel<",
     "attn_decode_split_kernel": "attn_decode_split_kernel<",
     "attn_decode_append_kernel": "attn_decode_append_kernel<",
-    "attn_bwd_dkdv_kernel": "attn_bwd_dkdv_kernel<",
+    "attn_bwd_dkdv": "attn_bwd_dkdv_",  # attn_bwd_dkdv_kernel (d = 64) or attn_bwd_dkdv_pair_kernel (d = 128)
     "attn_bwd_dq_kernel": "attn_bwd_dq_kernel<",
     "attn_fwd_fp8_kernel": "attn_fwd_fp8_kernel<",
     "attn_fp8_quant_kernel": "attn_fp8_quant_kernel<",
@@ -209,7 +209,7 @@ def time_backward(ea, pc, out, lse, stream, torch, digest, reps=10):
             "algorithmic_bytes": alg,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic_sum(["attn_bwd_dkdv_kernel", "attn_bwd_dq_kernel"], digest)},
+                         "traffic": traffic_sum(["attn_bwd_dkdv", "attn_bwd_dq_kernel"], digest)},
             "workload": PREFILL}
 
 
