@@ -186,9 +186,10 @@ __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
     for (int i = 0; i < 4; ++i) {
         lo[i] = hi[i] = 0u;
         if (!zero && kb * kFp8Block + r0 + i < p.n) {  // padding rows are code 0 (a turned zero row can hold -0)
-            lo[i] = cvt_fp8x2<false>(v[i][0] * inv, v[i][1] * inv, 0u);
+            // the second conversion overwrites bytes 2-3 of the first's seed
+            lo[i] = cvt_fp8x2<false>(v[i][0] * inv, v[i][1] * inv, __float_as_uint(v[i][0]));
             lo[i] = cvt_fp8x2<true>(v[i][2] * inv, v[i][3] * inv, lo[i]);
-            hi[i] = cvt_fp8x2<false>(v[i][4] * inv, v[i][5] * inv, 0u);
+            hi[i] = cvt_fp8x2<false>(v[i][4] * inv, v[i][5] * inv, __float_as_uint(v[i][4]));
             hi[i] = cvt_fp8x2<true>(v[i][6] * inv, v[i][7] * inv, hi[i]);
         }
     }
@@ -434,7 +435,9 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int kb = i >> 2, r0 = 4 * (i & 3);
-                uint32_t w = cvt_fp8x2<false>(sacc[kb][r0], sacc[kb][r0 + 1], 0u);
+                // bytes 2-3 of the first result are overwritten by the second,
+                // so any seed works; this one costs no register move
+                uint32_t w = cvt_fp8x2<false>(sacc[kb][r0], sacc[kb][r0 + 1], __float_as_uint(sacc[kb][r0]));
                 w = cvt_fp8x2<true>(sacc[kb][r0 + 2], sacc[kb][r0 + 3], w);
                 pb[i] = (int)w;
             }
