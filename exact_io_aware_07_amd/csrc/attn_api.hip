@@ -198,8 +198,8 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
     if (num_heads_q % num_heads_kv)
         return fail(ATTN_ERR_SHAPE, "num_heads_kv=%d does not divide num_heads_q=%d", num_heads_kv,
                     num_heads_q);
-    if (head_dim != 64 && head_dim != 128)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: head_dim=%d not in {64,128}", head_dim);
+    if (!head_dim_supported(head_dim))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: head_dim=%d not in {64,128,256}", head_dim);
     if (causal != 0 && causal != 1) return fail(ATTN_ERR_SHAPE, "causal must be 0 or 1 (got %d)", causal);
     attn_status_t st = check_scale(softmax_scale);
     if (st != ATTN_OK) return st;

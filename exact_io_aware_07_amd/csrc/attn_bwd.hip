@@ -40,7 +40,9 @@ __device__ __forceinline__ uint32_t swz_b(uint32_t row) {
     if constexpr (CH == 8) {
         return (((row >> 1) & 1u) << 2) | ((row >> 2) & 3u);  // 128-byte rows: odd rows use the other banks
     } else {
-        static_assert(CH == 16, "backward tiles support d = 64 and 128");
+        // 256- and 512-byte rows start on the same bank, so the low four
+        // slot bits alone decide the bank group.
+        static_assert(CH == 16 || CH == 32, "backward tiles support d = 64, 128 and 256");
         return ((row & 3u) << 2) | ((row >> 2) & 3u);
     }
 }
@@ -373,12 +375,14 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 // and K and V needs about 360): wave w (w < NP) forms S = Q K^T, the mask
 // and P = exp(S - lse), hands P to wave w + NP through LDS and accumulates
 // dV^T += G^T P; wave w + NP forms dP = G V^T, dS = P o (dP - D) and
-// accumulates dK^T += Q^T dS.  The two waves of a pair share a SIMD (waves w
-// and w + 4 of an 8-wave workgroup), so each one's vector work runs beside
-// the other's matrix products.  Same arithmetic and the same order of
-// accumulation per register as attn_bwd_dkdv_kernel.
-template <int D, int NP, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// accumulates dK^T += Q^T dS.  At d = 128 the two waves of a pair share a
+// SIMD (waves w and w + 4 of an 8-wave workgroup, two waves per SIMD), so
+// each one's vector work runs beside the other's matrix products; at d = 256
+// one accumulator and the K or V fragments alone take a wave's registers at
+// two waves per SIMD, so two pairs run at one wave per SIMD.  Same arithmetic
+// and the same order of accumulation per register as attn_bwd_dkdv_kernel.
+template <int D, int NP, int WPE, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bwd_dkdv_pair_kernel(BwdParams p) {
     constexpr int NW = 2 * NP;
     constexpr int QBLK = 64;       // query rows per LDS stage
@@ -717,7 +721,11 @@ void attn_bwd_dq_kernel(BwdParams p) {
 template <int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
     constexpr int DKDV_NW = 4, DKDV_WPE = 2;  // d = 64: two 4-wave workgroups per CU
-    constexpr int DQ_NW = 8, DQ_WPE = 2;
+    // d = 128: 4 pairs at two waves per SIMD; d = 256: 2 pairs at one.
+    constexpr int PAIR_NP = D == 256 ? 2 : 4, PAIR_WPE = D == 256 ? 1 : 2;
+    // dQ: 8 waves at two per SIMD; at d = 256 the Q, G and dQ registers of a
+    // 32-row wave take a SIMD's budget, so 4 waves at one per SIMD.
+    constexpr int DQ_NW = D == 256 ? 4 : 8, DQ_WPE = D == 256 ? 1 : 2;
     BwdParams p = p0;
     {
         const long waves = ((long)p.total_q + 15) / 16 * p.hq;  // 16 rows of one head per wave
@@ -728,16 +736,16 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     {
-        constexpr int KT = 32 * DKDV_NW;
+        constexpr int KT = 32 * (D >= 128 ? PAIR_NP : DKDV_NW);
         p.n_tiles = (p.max_k + KT - 1) / KT;
         const long grid = (long)p.n_tiles * p.batch * p.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         if (grid > 0) {
-            // d = 128: one wave per SIMD would hold both accumulators, so the
-            // work of each 32-key group is split over a pair of waves.
-            if constexpr (D == 128)
-                hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, DKDV_NW, CAUSAL, VARLEN>), dim3((unsigned)grid),
-                                   dim3(2 * DKDV_NW * 64), 0, s, p);
+            // d >= 128: one wave would hold both accumulators, so the work of
+            // each 32-key group is split over a pair of waves.
+            if constexpr (D >= 128)
+                hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<D, PAIR_NP, PAIR_WPE, CAUSAL, VARLEN>),
+                                   dim3((unsigned)grid), dim3(2 * PAIR_NP * 64), 0, s, p);
             else
                 hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DKDV_NW, DKDV_WPE, CAUSAL, VARLEN>),
                                    dim3((unsigned)grid), dim3(DKDV_NW * 64), 0, s, p);
@@ -767,6 +775,7 @@ hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, bool varlen
     switch (head_dim) {
         case 64: return launch_bwd_d<64>(p, causal, varlen, s);
         case 128: return launch_bwd_d<128>(p, causal, varlen, s);
+        case 256: return launch_bwd_d<256>(p, causal, varlen, s);
         default: return hipErrorInvalidValue;
     }
 }

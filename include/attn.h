@@ -235,8 +235,8 @@ attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void*
  * dq, dk, dv (bf16, written; round to nearest even) must not overlap any
  * input, the workspace or each other.  Calls that share a workspace on one
  * stream are ordered; on different streams they race.
- * Requirements: those of attn_fwd, and head_dim in {64, 128}
- * (ATTN_ERR_UNSUPPORTED otherwise); workspace_bytes too small gives
+ * Requirements: those of attn_fwd (head_dim in {64, 128, 256};
+ * ATTN_ERR_UNSUPPORTED otherwise); workspace_bytes too small gives
  * ATTN_ERR_SHAPE.  Errors are returned before anything is enqueued.
  */
 attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* out,

@@ -232,7 +232,7 @@ def bwd(**kw):
     (dict(ck=FAKE), 1),
     (dict(batch=0), 2), (dict(tq=0), 2), (dict(tq=9), 2), (dict(hq=6, hkv=4), 2), (dict(causal=3), 2),
     (dict(wsb=8 * 8 * 4 - 1), 2),
-    (dict(d=256), 3), (dict(d=96), 3),
+    (dict(d=32), 3), (dict(d=96), 3),
     (dict(scale=0.0), 4),
     (dict(dq=FAKE), 5), (dict(dk=FAKE3), 5), (dict(dv=DK), 5), (dict(ws=DQ), 5), (dict(dq=OUT), 5),
 ])

@@ -117,6 +117,9 @@ SMALL = [
     (1, 1, 1000, 8, 1, 128, True),     # one query row
     (1, 200, 200, 8, 2, 64, False),
     (2, 96, 33, 4, 4, 128, False),
+    (1, 128, 128, 2, 2, 256, True),
+    (2, 65, 200, 4, 2, 256, True),     # d = 256: ragged, GQA, bottom-right corner
+    (1, 257, 300, 3, 1, 256, False),   # d = 256: MQA, non-causal
 ]
 
 
@@ -134,7 +137,7 @@ def test_bwd_long_causal_sampled_heads():
     run_dense(1, 4096, 4096, 4, 4, 128, True, seed=41, heads=[0, 3])
 
 
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d", [128, 64, 256])
 def test_bwd_varlen(d):
     lens = [(3, 100), (0, 5), (64, 64), (129, 300), (1, 1), (70, 0)]
     nq = [a for a, _ in lens]

@@ -76,7 +76,7 @@ def test_decode_random(seed):
 def test_bwd_random(seed):
     from test_bwd_gpu import run_dense
     r = np.random.default_rng(3000 + seed)
-    d = int(r.choice([64, 128]))
+    d = int(r.choice([64, 128, 256]))
     hkv = int(r.integers(1, 3))
     hq = hkv * int(r.choice([1, 2, 4]))
     run_dense(int(r.integers(1, 3)), int(r.integers(1, 300)), int(r.integers(1, 300)), hq, hkv, d,
