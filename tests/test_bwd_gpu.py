@@ -137,6 +137,12 @@ def test_bwd_long_causal_sampled_heads():
     run_dense(1, 4096, 4096, 4, 4, 128, True, seed=41, heads=[0, 3])
 
 
+def test_bwd_prefill_workload_sampled():
+    """The shape and launch configuration bench.py times for the backward (B=4, H=16,
+    N=4096, d=128, causal): every batch of two heads checked against the oracle."""
+    run_dense(4, 4096, 4096, 16, 16, 128, True, seed=2, heads=[0, 9])
+
+
 @pytest.mark.parametrize("d", [128, 64, 256])
 def test_bwd_varlen(d):
     lens = [(3, 100), (0, 5), (64, 64), (129, 300), (1, 1), (70, 0)]
