@@ -95,15 +95,18 @@ __device__ __forceinline__ float lane_xor(float x) {
 
 // One cross-lane butterfly stage of the turn: the lane holding x[i] (bit M of
 // its chunk index clear) keeps x[i] + x[i+h], its partner x[i] - x[i+h].
+// other +- mine as one fused multiply-add with a +-1 factor: the product is
+// exact, so the single rounding gives the same bits as the add or subtract.
 template <int M>
 __device__ __forceinline__ void xstage(float (&v)[4][8], bool low) {
+    const float sgn = low ? 1.0f : -1.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float mine = v[i][e];
             const float other = lane_xor<M>(mine);
-            v[i][e] = low ? mine + other : other - mine;
+            v[i][e] = __builtin_fmaf(mine, sgn, other);
         }
 }
 
