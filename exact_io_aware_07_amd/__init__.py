@@ -473,10 +473,11 @@ def attn_fp8_num_blocks(seqlen):
 
 
 def attn_fp8_quantize(x, *, signs=None, layout="rows", codes=None, scales=None, stream=None):
-    """Block-quantise x [B, N, H, 128] bf16 to E4M3 codes (uint8) and float32
-    block scales [B, H, ceil(N / 64)].  signs: int8 [128] of +-1 to turn the
-    rows first (Q and K), or None.  layout "rows": codes [B, N, H, 128];
-    "vt": codes [B, H, 128, Np] in the V^T layout attn_fwd_fp8 reads."""
+    """Block-quantise x [B, N, H, d] bf16 (d in {64, 128, 256}) to E4M3 codes
+    (uint8) and float32 block scales [B, H, ceil(N / 64)].  signs: int8 [d] of
+    +-1 to turn the rows first (Q and K), or None.  layout "rows": codes
+    [B, N, H, d]; "vt": codes [B, H, d, Np] in the V^T layout attn_fwd_fp8
+    reads."""
     dev = x.device
     _need(x, "x", torch.bfloat16, dev)
     if x.dim() != 4:
@@ -506,9 +507,9 @@ def attn_fp8_quantize(x, *, signs=None, layout="rows", codes=None, scales=None, 
 
 def attn_fwd_fp8(q_codes, k_codes, v_codes_t, q_scales, k_scales, v_scales, *, causal, softmax_scale,
                  incoherent, out=None, lse=None, return_lse=True, stream=None):
-    """Attention forward on attn_fp8_quantize's codes: q [B, Nq, Hq, 128] and
-    k [B, Nk, Hkv, 128] in the row layout, v in the V^T layout
-    [B, Hkv, 128, Np].  Returns (out [B, Nq, Hq, 128] bf16, lse [B, Hq, Nq])."""
+    """Attention forward on attn_fp8_quantize's codes: q [B, Nq, Hq, d] and
+    k [B, Nk, Hkv, d] in the row layout, v in the V^T layout [B, Hkv, d, Np]
+    (d in {64, 128, 256}).  Returns (out [B, Nq, Hq, d] bf16, lse [B, Hq, Nq])."""
     dev = q_codes.device
     for t, n in ((q_codes, "q_codes"), (k_codes, "k_codes"), (v_codes_t, "v_codes_t")):
         _need(t, n, torch.uint8, dev)
@@ -541,7 +542,7 @@ def attn_fwd_fp8(q_codes, k_codes, v_codes_t, q_scales, k_scales, v_scales, *, c
 
 
 def attn_fp8_forward(q, k, v, *, causal, softmax_scale, signs=None, stream=None):
-    """Quantise bf16 q, k, v ([B, N, H, 128]) and run attn_fwd_fp8: Q and K turned
+    """Quantise bf16 q, k, v ([B, N, H, d]) and run attn_fwd_fp8: Q and K turned
     by `signs` (incoherent processing) when given.  Returns (out, lse)."""
     qc, qs = attn_fp8_quantize(q, signs=signs, layout="rows", stream=stream)
     kc, ks = attn_fp8_quantize(k, signs=signs, layout="rows", stream=stream)

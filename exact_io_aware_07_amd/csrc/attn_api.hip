@@ -484,7 +484,8 @@ attn_status_t attn_fp8_quantize(const void* x, const int8_t* signs, int batch, i
         return fail(ATTN_ERR_SHAPE, "counts out of range: batch=%d seqlen=%d num_heads=%d", batch, seqlen,
                     num_heads);
     if (layout != 0 && layout != 1) return fail(ATTN_ERR_SHAPE, "layout must be 0 (rows) or 1 (V^T)");
-    if (head_dim != 128) return fail(ATTN_ERR_UNSUPPORTED, "FP8 path: head_dim must be 128 (got %d)", head_dim);
+    if (!head_dim_supported(head_dim))
+        return fail(ATTN_ERR_UNSUPPORTED, "FP8 path: head_dim=%d not in {64,128,256}", head_dim);
     const size_t xb = (size_t)batch * seqlen * num_heads * head_dim * 2;
     const size_t cb = attn_fp8_codes_bytes(batch, seqlen, num_heads, head_dim, layout);
     const size_t sb = (size_t)batch * num_heads * attn_fp8_num_blocks(seqlen) * 4;
@@ -499,7 +500,7 @@ attn_status_t attn_fp8_quantize(const void* x, const int8_t* signs, int batch, i
     p.batch = batch;
     p.n = seqlen;
     p.heads = num_heads;
-    return hip_status(attn::launch_fp8_quant(p, layout == 1, static_cast<hipStream_t>(stream)),
+    return hip_status(attn::launch_fp8_quant(p, head_dim, layout == 1, static_cast<hipStream_t>(stream)),
                       "attn_fp8_quantize launch");
 }
 
@@ -520,7 +521,8 @@ attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void*
                     num_heads_q);
     if ((causal != 0 && causal != 1) || (incoherent != 0 && incoherent != 1))
         return fail(ATTN_ERR_SHAPE, "causal and incoherent must be 0 or 1");
-    if (head_dim != 128) return fail(ATTN_ERR_UNSUPPORTED, "FP8 path: head_dim must be 128 (got %d)", head_dim);
+    if (!head_dim_supported(head_dim))
+        return fail(ATTN_ERR_UNSUPPORTED, "FP8 path: head_dim=%d not in {64,128,256}", head_dim);
     attn_status_t st = check_scale(softmax_scale);
     if (st != ATTN_OK) return st;
     const size_t ob = (size_t)batch * seqlen_q * num_heads_q * head_dim * 2;
@@ -536,7 +538,7 @@ attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void*
         if (overlap(out, ob, ins[i], inb[i]) || overlap(lse, lb, ins[i], inb[i]))
             return fail(ATTN_ERR_ALIAS, "out/lse overlap an input");
     if (overlap(out, ob, lse, lb)) return fail(ATTN_ERR_ALIAS, "out and lse overlap");
-    if (128L * attn_fp8_num_blocks(seqlen_k) * 64 > 0xffffffffL)
+    if ((long)head_dim * attn_fp8_num_blocks(seqlen_k) * 64 > 0xffffffffL)
         return fail(ATTN_ERR_UNSUPPORTED, "seqlen_k too large for 32-bit tile offsets");
     attn::Fp8FwdParams p{};
     p.q = static_cast<const uint8_t*>(q_codes);
@@ -556,7 +558,7 @@ attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void*
     p.nbq = attn_fp8_num_blocks(seqlen_q);
     p.nbk = attn_fp8_num_blocks(seqlen_k);
     p.scale = incoherent ? softmax_scale / (float)head_dim : softmax_scale;
-    return hip_status(attn::launch_fwd_fp8(p, causal != 0, static_cast<hipStream_t>(stream)),
+    return hip_status(attn::launch_fwd_fp8(p, head_dim, causal != 0, static_cast<hipStream_t>(stream)),
                       "attn_fwd_fp8 launch");
 }
 

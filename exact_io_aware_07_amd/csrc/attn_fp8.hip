@@ -1,5 +1,5 @@
 // FP8 forward pass: block quantisation with incoherent processing, and the
-// attention kernel on E4M3 operands (gfx950, head_dim 128).
+// attention kernel on E4M3 operands (gfx950, head_dim 64, 128 or 256).
 //
 // "FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels (2026)",
 // "FlashAttention-3": FP8 with one scale per block and incoherent processing
@@ -20,11 +20,11 @@
 //           code = E4M3(x * (448 / amax)) with the product rounded to float32;
 //           a zero block has scale 0 and codes 0
 //   turn    x -> H (s * x) along d for Q and K: unnormalised Walsh-Hadamard
-//           butterflies in float32, stage h = 1, 2, 4, ..., 64, the pair
+//           butterflies in float32, stage h = 1, 2, 4, ..., d / 2, the pair
 //           (x[i], x[i+h]), i & h == 0, becoming (x[i] + x[i+h], x[i] - x[i+h]);
 //           scores of turned operands are d times the original ones
-//   Q, K    codes [B, N, H, 128] (row layout)
-//   V       codes [B, H, 128, Np] (V^T layout, Np = N rounded up to 64): inside
+//   Q, K    codes [B, N, H, d] (row layout)
+//   V       codes [B, H, d, Np] (V^T layout, Np = N rounded up to 64): inside
 //           every 64-key block, byte p = 32 h + 16 kb + 4 g + e holds key
 //           32 kb + 8 g + 4 h + e, the order in which a lane holds the keys of
 //           a score tile; padding keys are zero codes
@@ -37,7 +37,6 @@ namespace attn {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kFp8D = 128;
 constexpr int kFp8Block = 64;
 constexpr float kE4M3Max = 448.0f;
 // The attention kernel's shift is raised only when a tile's maximum exceeds it
@@ -97,6 +96,7 @@ __device__ __forceinline__ float lane_xor(float x) {
 // its chunk index clear) keeps x[i] + x[i+h], its partner x[i] - x[i+h].
 // other +- mine as one fused multiply-add with a +-1 factor: the product is
 // exact, so the single rounding gives the same bits as the add or subtract.
+// (M = 16, the partner 16 lanes away, is xstage16.)
 template <int M>
 __device__ __forceinline__ void xstage(float (&v)[4][8], bool low) {
     const float sgn = low ? 1.0f : -1.0f;
@@ -110,29 +110,48 @@ __device__ __forceinline__ void xstage(float (&v)[4][8], bool low) {
         }
 }
 
-// One workgroup (256 threads) per (64-row block, head, sequence).  Thread t
-// holds rows 4 (t / 16) .. + 3 of the block, values 8 (t % 16) .. + 7 of each:
-// a row's 128 values lie on 16 consecutive lanes (the butterflies' partners),
-// and four consecutive rows are four consecutive keys of a V^T word.
-template <bool VT>
-__global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
+// The cross-lane stage with the partner 16 lanes away (d = 256):
+// v_permlane16_swap of x with itself returns {x[l], x[l ^ 16]} in lanes of
+// even 16-lane rows (bit 4 of the chunk index clear) and {x[l ^ 16], x[l]} in
+// odd ones, so r0 + sgn * r1 is own + partner there and partner - own here.
+__device__ __forceinline__ void xstage16(float (&v)[4][8], bool low) {
+    const float sgn = low ? 1.0f : -1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i][e]), __float_as_uint(v[i][e]),
+                                                            false, false);
+            v[i][e] = __builtin_fmaf(__uint_as_float(r[1]), sgn, __uint_as_float(r[0]));
+        }
+}
+
+// One workgroup (2 d threads) per (64-row block, head, sequence).  With
+// L = d / 8 lanes per row, thread t holds rows 4 (t / L) .. + 3 of the block,
+// values 8 (t % L) .. + 7 of each: a row's d values lie on L consecutive
+// lanes (the butterflies' partners), and four consecutive rows are four
+// consecutive keys of a V^T word.
+template <int D, bool VT>
+__global__ __launch_bounds__(2 * D) void attn_fp8_quant_kernel(Fp8QuantParams p) {
 #pragma clang fp contract(off)
-    __shared__ float wmax[4];
-    __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? kFp8D * kFp8Block : 16];
+    constexpr int L = D / 8;         // lanes per row
+    constexpr int NWQ = 2 * D / 64;  // waves per workgroup
+    __shared__ float wmax[NWQ];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? D * kFp8Block : 16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nblk = (p.n + kFp8Block - 1) / kFp8Block;
     const int kb = blockIdx.x % nblk;
     const int bh = blockIdx.x / nblk;
     const int h = bh % p.heads, b = bh / p.heads;
-    const int j = tid & 15;          // 8-value chunk of the rows
-    const int r0 = 4 * (tid >> 4);   // first of this thread's four rows
+    const int j = tid & (L - 1);  // 8-value chunk of the rows
+    const int r0 = 4 * (tid / L);  // first of this thread's four rows
 
     u32x4 raw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int n = kb * kFp8Block + r0 + i;
         raw[i] = u32x4{0u, 0u, 0u, 0u};
-        if (n < p.n) raw[i] = load16(p.x + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j);
+        if (n < p.n) raw[i] = load16(p.x + (((long)b * p.n + n) * p.heads + h) * D + 8 * j);
     }
     float sg[8];
     if (p.signs != nullptr) {
@@ -164,11 +183,12 @@ __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
                         v[i][e + hs] = a - c;
                     }
         }
-        // cross-lane stages h = 8, 16, 32, 64: partner chunk j ^ (h / 8)
+        // cross-lane stages h = 8, 16, ..., d / 2: partner chunk j ^ (h / 8)
         xstage<1>(v, (j & 1) == 0);
         xstage<2>(v, (j & 2) == 0);
         xstage<4>(v, (j & 4) == 0);
-        xstage<8>(v, (j & 8) == 0);
+        if constexpr (L > 8) xstage<8>(v, (j & 8) == 0);
+        if constexpr (L > 16) xstage16(v, (j & 16) == 0);
     }
     float amax = 0.0f;
 #pragma unroll
@@ -178,7 +198,9 @@ __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
     amax = wave_max_f(amax);
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < NWQ; ++w) amax = fmaxf(amax, wmax[w]);
     const bool zero = !(amax > 0.0f);
     const float inv = zero ? 0.0f : kE4M3Max / amax;
     if (tid == 0) p.scales[(long)bh * nblk + kb] = zero ? 0.0f : amax / kE4M3Max;
@@ -201,7 +223,7 @@ __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
         for (int i = 0; i < 4; ++i) {
             const int n = kb * kFp8Block + r0 + i;
             if (n < p.n)
-                *reinterpret_cast<u32x2*>(p.codes + (((long)b * p.n + n) * p.heads + h) * kFp8D + 8 * j) =
+                *reinterpret_cast<u32x2*>(p.codes + (((long)b * p.n + n) * p.heads + h) * D + 8 * j) =
                     u32x2{lo[i], hi[i]};
         }
     } else {
@@ -226,23 +248,33 @@ __global__ __launch_bounds__(256) void attn_fp8_quant_kernel(Fp8QuantParams p) {
         const int np = nblk * kFp8Block;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i;        // 16-byte chunk of the 128 x 64 tile
+            const int c = tid + 2 * D * i;      // 16-byte chunk of the d x 64 tile
             const int dd = c >> 2, q = c & 3;
             const u32x4 w = *reinterpret_cast<const u32x4*>(tile + dd * kFp8Block + 16 * q);
-            *reinterpret_cast<u32x4*>(p.codes + ((long)bh * kFp8D + dd) * np + (long)kb * kFp8Block + 16 * q) = w;
+            *reinterpret_cast<u32x4*>(p.codes + ((long)bh * D + dd) * np + (long)kb * kFp8Block + 16 * q) = w;
         }
     }
 }
 
-hipError_t launch_fp8_quant(const Fp8QuantParams& p, bool vt, hipStream_t s) {
+template <int D>
+static void launch_fp8_quant_d(const Fp8QuantParams& p, bool vt, unsigned grid, hipStream_t s) {
+    if (vt)
+        hipLaunchKernelGGL((attn_fp8_quant_kernel<D, true>), dim3(grid), dim3(2 * D), 0, s, p);
+    else
+        hipLaunchKernelGGL((attn_fp8_quant_kernel<D, false>), dim3(grid), dim3(2 * D), 0, s, p);
+}
+
+hipError_t launch_fp8_quant(const Fp8QuantParams& p, int head_dim, bool vt, hipStream_t s) {
     const long nblk = (p.n + kFp8Block - 1) / kFp8Block;
     const long grid = nblk * p.batch * p.heads;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    if (vt)
-        hipLaunchKernelGGL(attn_fp8_quant_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL(attn_fp8_quant_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, p);
+    switch (head_dim) {
+        case 64: launch_fp8_quant_d<64>(p, vt, (unsigned)grid, s); break;
+        case 128: launch_fp8_quant_d<128>(p, vt, (unsigned)grid, s); break;
+        case 256: launch_fp8_quant_d<256>(p, vt, (unsigned)grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -258,12 +290,16 @@ hipError_t launch_fp8_quant(const Fp8QuantParams& p, bool vt, hipStream_t s) {
 // <= 4; they are multiplied by 64 * s_v(t) / max_t s_v(t) (folded into the
 // exponent), which puts the V tile scale into P and keeps the E4M3 values
 // <= 256; the row sum is kept from the unrounded values.
-template <bool CAUSAL, int NW, int WPE>
+template <int D, bool CAUSAL, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     constexpr int BR = NW * 32, BC = 64;
-    static_assert(8 % NW == 0, "each wave issues the same number of tile loads");
-    constexpr uint32_t K_BYTES = BC * kFp8D, STAGE = 2 * K_BYTES;
+    constexpr int KSD = D / 64;   // 64-wide d steps of S^T
+    constexpr int DBD = D / 32;   // 32-row d blocks of O^T
+    constexpr int KCH = D / 16;   // 16-byte chunks per K row
+    constexpr int NI = D / 16;    // one-KiB loads per tensor and tile
+    static_assert(NI % NW == 0, "each wave issues the same number of tile loads");
+    constexpr uint32_t K_BYTES = BC * D, STAGE = 2 * K_BYTES;
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
 
@@ -301,9 +337,9 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     const int w_last_row = min(wr0 + 32, Nq) - 1;
     const int w_hi_max = hi_of(w_last_row), w_hi_min = hi_of(wr0);
 
-    const uint32_t stride_k = (uint32_t)(p.hkv * kFp8D);  // bytes between key rows
-    const uint8_t* kbase = p.k + ((long)b * Nk * p.hkv + kvh) * kFp8D;
-    const uint8_t* vtbase = p.vt + ((long)b * p.hkv + kvh) * kFp8D * (long)p.np;
+    const uint32_t stride_k = (uint32_t)(p.hkv * D);  // bytes between key rows
+    const uint8_t* kbase = p.k + ((long)b * Nk * p.hkv + kvh) * D;
+    const uint8_t* vtbase = p.vt + ((long)b * p.hkv + kvh) * D * (long)p.np;
     const float* ks_row = p.k_scale + ((long)b * p.hkv + kvh) * p.nbk;
     const float* vs_row = p.v_scale + ((long)b * p.hkv + kvh) * p.nbk;
 
@@ -312,13 +348,13 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
         const int nvalid = Nk - key0;
         const uint32_t nrec = nvalid > 0 ? (uint32_t)(nvalid < BC ? nvalid : BC) * stride_k : 0u;
         const u32x4 rk = rsrc_words(kbase + (long)key0 * stride_k, nrec);
-        const u32x4 rv = rsrc_words(vtbase + key0, 127u * (uint32_t)p.np + (uint32_t)BC);
-        // each tile is 8 KiB of K and 8 KiB of V^T: 8 one-KiB loads of each
+        const u32x4 rv = rsrc_words(vtbase + key0, (uint32_t)(D - 1) * (uint32_t)p.np + (uint32_t)BC);
+        // each tile is 64 d bytes of K and as many of V^T: d / 16 one-KiB loads of each
 #pragma unroll
-        for (int jj = 0; jj < 8 / NW; ++jj) {
-            const int i = wave * (8 / NW) + jj;
-            const uint32_t krow = 8 * i + (lane >> 3), kc = lane & 7;
-            dma16(rk, st + 1024 * i, krow * stride_k + ((kc ^ swz<8>(krow)) * 16));
+        for (int jj = 0; jj < NI / NW; ++jj) {
+            const int i = wave * (NI / NW) + jj;
+            const uint32_t krow = (1024 / D) * i + lane / KCH, kc = lane % KCH;
+            dma16(rk, st + 1024 * i, krow * stride_k + ((kc ^ swz<KCH>(krow)) * 16));
             const uint32_t vrow = 16 * i + (lane >> 2), vc = lane & 3;
             dma16(rv, st + K_BYTES + 1024 * i, vrow * (uint32_t)p.np + ((vc ^ swz<4>(vrow)) * 16));
         }
@@ -326,12 +362,12 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
 
     // Q^T fragments (B operand): lane half h holds d = 64 s + 32 h .. + 31 of its row.
     const int row = wr0 + l32;
-    i32x8 qf[2];
+    i32x8 qf[KSD];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < KSD; ++s) {
         u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
         if (row < Nq) {
-            const uint8_t* qrow = p.q + (((long)b * Nq + row) * p.hq + hq) * kFp8D + 64 * s + 32 * h;
+            const uint8_t* qrow = p.q + (((long)b * Nq + row) * p.hq + hq) * D + 64 * s + 32 * h;
             a = *reinterpret_cast<const u32x4*>(qrow);
             c = *reinterpret_cast<const u32x4*>(qrow + 16);
         }
@@ -345,9 +381,9 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     const float log2_svmax = svmax > 0.0f ? __log2f(svmax) : 0.0f;
     const float c2q = p.scale * kLog2e * s_q;
 
-    f32x16 oacc[4];
+    f32x16 oacc[DBD];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DBD; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     float m_run = -INFINITY, l_part = 0.0f;
@@ -382,13 +418,13 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < KSD; ++s)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const uint32_t kr = 32 * kb + l32;
                     const uint32_t c0 = 4 * s + 2 * h;
-                    const u32x4 a0 = lds_read16(ks, kr * kFp8D + ((c0 ^ swz<8>(kr)) * 16));
-                    const u32x4 a1 = lds_read16(ks, kr * kFp8D + (((c0 + 1) ^ swz<8>(kr)) * 16));
+                    const u32x4 a0 = lds_read16(ks, kr * D + ((c0 ^ swz<KCH>(kr)) * 16));
+                    const u32x4 a1 = lds_read16(ks, kr * D + (((c0 + 1) ^ swz<KCH>(kr)) * 16));
                     const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                      (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
                     sacc[kb] = mfma_fp8(a, qf[s], sacc[kb]);
@@ -414,7 +450,7 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
                 const float alpha = (raise && m_run != -INFINITY) ? exp2f(m_run - mx) : 1.0f;
                 l_part *= alpha;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                for (int db = 0; db < DBD; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
             }
@@ -445,7 +481,7 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
                 pb[i] = (int)w;
             }
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
+            for (int db = 0; db < DBD; ++db) {
                 const uint32_t vr = 32 * db + l32;
                 const u32x4 a0 = lds_read16(vs, vr * BC + (((2 * h) ^ swz<4>(vr)) * 16));
                 const u32x4 a1 = lds_read16(vs, vr * BC + (((2 * h + 1) ^ swz<4>(vr)) * 16));
@@ -467,9 +503,9 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     const float l_tot = pair_sum(l_part);
     if (row < Nq) {
         const float inv = l_tot > 0.0f ? vref / (exp2f(kFp8PScale) * l_tot) : 0.0f;
-        uint16_t* orow = p.out + (((long)b * Nq + row) * p.hq + hq) * kFp8D;
+        uint16_t* orow = p.out + (((long)b * Nq + row) * p.hq + hq) * D;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < DBD; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 w = {pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
@@ -482,26 +518,50 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     }
 }
 
-// Four-wave workgroups (128 query rows) at three waves per SIMD (168 VGPRs):
+// Four-wave workgroups (128 query rows) at three waves per SIMD (d <= 128):
 // the softmax's vector work limits this kernel, and a third wave per SIMD
 // hides more of it than 8-wave workgroups at two per SIMD (measured +12% on
-// the causal 4096-token workload, although each tile is loaded by twice as
-// many workgroups).
-constexpr int kFp8NW = 4, kFp8WPE = 3;
+// the causal 4096-token workload at d = 128, although each tile is loaded by
+// twice as many workgroups).  At d = 256 eight-wave workgroups (256 query
+// rows, two waves per SIMD) fit the 256-register budget without spills and
+// run 1.7x faster than four waves at one per SIMD on that workload (a second
+// wave per SIMD hides the softmax; a four-wave workgroup at two per SIMD
+// spills).
+#ifndef ATTN_FP8_CFG64
+#define ATTN_FP8_CFG64 4, 3
+#endif
+#ifndef ATTN_FP8_CFG128
+#define ATTN_FP8_CFG128 4, 3
+#endif
+#ifndef ATTN_FP8_CFG256
+#define ATTN_FP8_CFG256 8, 2
+#endif
+template <int D> struct Fp8Cfg;  // {waves per workgroup, waves per SIMD}
+template <> struct Fp8Cfg<64> { static constexpr int v[2] = {ATTN_FP8_CFG64}; };
+template <> struct Fp8Cfg<128> { static constexpr int v[2] = {ATTN_FP8_CFG128}; };
+template <> struct Fp8Cfg<256> { static constexpr int v[2] = {ATTN_FP8_CFG256}; };
 
-hipError_t launch_fwd_fp8(const Fp8FwdParams& p0, bool causal, hipStream_t s) {
-    Fp8FwdParams p = p0;
-    p.n_qtiles = (p.nq + 32 * kFp8NW - 1) / (32 * kFp8NW);
+template <int D>
+static hipError_t launch_fwd_fp8_d(Fp8FwdParams p, bool causal, hipStream_t s) {
+    constexpr int NW = Fp8Cfg<D>::v[0], WPE = Fp8Cfg<D>::v[1];
+    p.n_qtiles = (p.nq + 32 * NW - 1) / (32 * NW);
     const long grid = (long)p.n_qtiles * p.batch * p.hq;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (causal)
-        hipLaunchKernelGGL((attn_fwd_fp8_kernel<true, kFp8NW, kFp8WPE>), dim3((unsigned)grid), dim3(64 * kFp8NW), 0,
-                           s, p);
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, true, NW, WPE>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     else
-        hipLaunchKernelGGL((attn_fwd_fp8_kernel<false, kFp8NW, kFp8WPE>), dim3((unsigned)grid), dim3(64 * kFp8NW), 0,
-                           s, p);
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, false, NW, WPE>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int head_dim, bool causal, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_fwd_fp8_d<64>(p, causal, s);
+        case 128: return launch_fwd_fp8_d<128>(p, causal, s);
+        case 256: return launch_fwd_fp8_d<256>(p, causal, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace attn

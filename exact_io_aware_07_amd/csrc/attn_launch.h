@@ -87,20 +87,20 @@ struct BwdParams {
 struct Fp8QuantParams {
     const uint16_t* x;
     const int8_t* signs;  // +-1 per feature: turn by H(s * x) first; null: no turn
-    uint8_t* codes;       // row layout [batch, n, heads, 128] or V^T layout [batch, heads, 128, np]
+    uint8_t* codes;       // row layout [batch, n, heads, d] or V^T layout [batch, heads, d, np]
     float* scales;        // [batch, heads, ceil(n / 64)]
     int batch, n, heads;
 };
 
-// FP8 attention forward (dense, head_dim 128).
+// FP8 attention forward (dense, head_dim d in {64, 128, 256}).
 struct Fp8FwdParams {
-    const uint8_t* q;   // [batch, nq, hq, 128]
-    const uint8_t* k;   // [batch, nk, hkv, 128]
-    const uint8_t* vt;  // [batch, hkv, 128, np]
+    const uint8_t* q;   // [batch, nq, hq, d]
+    const uint8_t* k;   // [batch, nk, hkv, d]
+    const uint8_t* vt;  // [batch, hkv, d, np]
     const float* q_scale;  // [batch, hq, nbq]
     const float* k_scale;  // [batch, hkv, nbk]
     const float* v_scale;  // [batch, hkv, nbk]
-    uint16_t* out;      // [batch, nq, hq, 128] bf16
+    uint16_t* out;      // [batch, nq, hq, d] bf16
     float* lse;         // [batch, hq, nq] or null
     int batch, nq, nk, hq, hkv;
     int n_qtiles;       // filled in by the launcher
@@ -109,8 +109,8 @@ struct Fp8FwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, bool paged, hipStream_t s);
-hipError_t launch_fp8_quant(const Fp8QuantParams& p, bool vt, hipStream_t s);
-hipError_t launch_fwd_fp8(const Fp8FwdParams& p, bool causal, hipStream_t s);
+hipError_t launch_fp8_quant(const Fp8QuantParams& p, int head_dim, bool vt, hipStream_t s);
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, int head_dim, bool causal, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int head_dim, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_decode_split(const DecodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_decode_combine(const CombineParams& p, int head_dim, hipStream_t s);

@@ -170,8 +170,8 @@ attn_status_t attn_fwd_ex(const void* q, const void* k, const void* v,
  *           amax = max |x| (after the turn), scale = amax / 448 and code =
  *           E4M3(x * (448 / amax)) with the product rounded to float32; a
  *           block of zeros gets scale 0 and codes 0.  value ~ code * scale.
- * Requirements: head_dim == 128 (ATTN_ERR_UNSUPPORTED), positive counts,
- * layout 0 or 1 (ATTN_ERR_SHAPE); codes and scales must not overlap x, signs
+ * Requirements: head_dim in {64, 128, 256} (ATTN_ERR_UNSUPPORTED), positive
+ * counts, layout 0 or 1 (ATTN_ERR_SHAPE); codes and scales must not overlap x, signs
  * or each other (ATTN_ERR_ALIAS).
  */
 attn_status_t attn_fp8_quantize(const void* x, const int8_t* signs, int batch, int seqlen, int num_heads,
@@ -189,13 +189,13 @@ int attn_fp8_num_blocks(int seqlen);
  * dequantised to fp32 for the softmax; the online softmax is that of
  * attn_fwd).
  *
- *   q_codes, k_codes  layout 0 codes of Q [batch, seqlen_q, num_heads_q, 128]
- *                     and K [batch, seqlen_k, num_heads_kv, 128]
- *   v_codes_t         layout 1 codes of V [batch, num_heads_kv, 128, Np]
+ *   q_codes, k_codes  layout 0 codes of Q [batch, seqlen_q, num_heads_q, d]
+ *                     and K [batch, seqlen_k, num_heads_kv, d], d = head_dim
+ *   v_codes_t         layout 1 codes of V [batch, num_heads_kv, d, Np]
  *   q/k/v_scales      their block scales
  *   incoherent        1 if Q and K were turned (same signs): the scores of the
  *                     turned operands are d times the original ones, so
- *                     softmax_scale / 128 is applied
+ *                     softmax_scale / d is applied
  *   out, lse          as attn_fwd in dense mode (bf16 out, float32 lse in
  *                     nats, lse may be NULL); causal masks align bottom-right
  * The probabilities are rounded to E4M3 for the P V product, after scaling by
@@ -205,7 +205,8 @@ int attn_fp8_num_blocks(int seqlen);
  * sums use the unrounded values.  Results equal exact attention on the
  * dequantised operands within the error of that rounding (2^-4 relative per
  * probability, 2^-10 absolute below 2^-6).
- * Requirements: head_dim == 128; others as attn_fwd.
+ * Requirements: head_dim in {64, 128, 256} (ATTN_ERR_UNSUPPORTED); others as
+ * attn_fwd.
  */
 attn_status_t attn_fwd_fp8(const void* q_codes, const void* k_codes, const void* v_codes_t,
                            const float* q_scales, const float* k_scales, const float* v_scales, int batch,

@@ -175,7 +175,7 @@ def fp8q(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(x=NULL), 1), (dict(codes=NULL), 1), (dict(scales=NULL), 1),
     (dict(batch=0), 2), (dict(n=0), 2), (dict(h=-1), 2), (dict(layout=2), 2),
-    (dict(d=64), 3), (dict(d=256, layout=1), 3),
+    (dict(d=32), 3), (dict(d=96, layout=1), 3), (dict(d=512), 3),
     (dict(codes=_at(0)), 5), (dict(scales=ctypes.c_void_p(0x1000000 + 100)), 5), (dict(signs=_at(1)), 5),
     (dict(scales=ctypes.c_void_p(0x2000000 + 64)), 5),
 ])
@@ -195,7 +195,7 @@ def fp8f(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=NULL), 1), (dict(v=NULL), 1), (dict(vs=NULL), 1), (dict(out=NULL), 1),
     (dict(batch=0), 2), (dict(nk=0), 2), (dict(hq=6, hkv=4), 2), (dict(causal=2), 2), (dict(inc=-1), 2),
-    (dict(d=64), 3), (dict(scale=0.0), 4), (dict(scale=float("inf")), 4),
+    (dict(d=32), 3), (dict(d=192), 3), (dict(scale=0.0), 4), (dict(scale=float("inf")), 4),
     (dict(out=_at(0)), 5), (dict(lse=_at(5)), 5), (dict(lse=ctypes.c_void_p(0x7000000 + 8)), 5),
 ])
 def test_fwd_fp8_rejects(kw, code):

@@ -28,17 +28,22 @@ def np_bf16(shape, seed, scale=1.0):
     return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("N,H,turn,layout", [(130, 3, False, "rows"), (130, 3, True, "rows"), (200, 2, False, "vt"),
-                                             (64, 1, True, "vt"), (1, 2, False, "rows"), (65, 2, True, "vt"),
-                                             (300, 2, True, "rows")],
-                         ids=lambda x: str(x))
-def test_quantize_bit_exact(N, H, turn, layout):
-    x = np_bf16((2, N, H, 128), seed=N + H)
+QUANT_CASES = [(130, 3, False, "rows", 128), (130, 3, True, "rows", 128), (200, 2, False, "vt", 128),
+               (64, 1, True, "vt", 128), (1, 2, False, "rows", 128), (65, 2, True, "vt", 128),
+               (300, 2, True, "rows", 128),
+               (130, 3, True, "rows", 64), (200, 2, False, "vt", 64), (65, 2, True, "vt", 64),
+               (130, 3, True, "rows", 256), (200, 2, False, "vt", 256), (65, 2, True, "vt", 256),
+               (1, 1, True, "rows", 256)]
+
+
+@pytest.mark.parametrize("N,H,turn,layout,d", QUANT_CASES, ids=lambda x: str(x))
+def test_quantize_bit_exact(N, H, turn, layout, d):
+    x = np_bf16((2, N, H, d), seed=N + H + d)
     if N >= 128:
         x[0, 64:128, 0] = 0.0            # a zero block
         x[1, 64:128, 1 % H] *= 1e-3      # a quiet block
         x[1, 70, 0, 5] = 300.0           # an outlier
-    signs = W.hadamard_signs(128, seed=N) if turn else None
+    signs = W.hadamard_signs(d, seed=N) if turn else None
     codes, scales = ea.attn_fp8_quantize(x.to(DEV), signs=None if signs is None else signs.to(DEV), layout=layout)
     torch.cuda.synchronize()
     ref_c, ref_s = OF.quantize_blocks(to64(x), None if signs is None else signs.numpy().astype(np.float64))
@@ -52,7 +57,7 @@ def test_quantize_bit_exact(N, H, turn, layout):
 
 def check_fp8(case, causal, turn, seed, rows=None):
     """Run the FP8 path on a dense case and compare with the oracle (all rows, or sampled rows)."""
-    d = 128
+    d = case["q"].shape[-1]
     scale = d ** -0.5
     signs = W.hadamard_signs(d, seed) if turn else None
     q, k, v = (case[x] for x in "qkv")
@@ -116,6 +121,28 @@ def test_fwd_fp8_small(shape):
     B, Nq, Nk, Hq, Hkv, causal, turn = shape
     case = W.dense_case(B, Nq, Nk, Hq, Hkv, 128, seed=Nq + 3 * Nk)
     check_fp8(case, causal, turn, seed=Nq)
+
+
+SHAPES_D = [
+    # (B, Nq, Nk, Hq, Hkv, d, causal, incoherent)
+    (1, 128, 128, 2, 2, 64, True, True),
+    (2, 200, 333, 4, 2, 64, True, False),
+    (1, 700, 65, 2, 1, 64, True, True),
+    (1, 513, 1030, 2, 2, 64, False, True),
+    (1, 128, 128, 2, 2, 256, True, True),
+    (2, 200, 333, 4, 2, 256, True, False),
+    (1, 700, 65, 2, 1, 256, True, True),
+    (1, 100, 30, 2, 2, 256, True, True),
+    (1, 513, 1030, 2, 2, 256, False, True),
+    (1, 1, 900, 8, 2, 256, True, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_D, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_fp8_head_dims(shape):
+    B, Nq, Nk, Hq, Hkv, d, causal, turn = shape
+    case = W.dense_case(B, Nq, Nk, Hq, Hkv, d, seed=Nq + 3 * Nk + d)
+    check_fp8(case, causal, turn, seed=Nq + d)
 
 
 def test_fwd_fp8_key_outliers_and_quiet_tiles():
