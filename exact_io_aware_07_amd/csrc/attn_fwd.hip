@@ -35,6 +35,14 @@ constexpr int kFwdPage = 256;
 #define ATTN_FWD_K_LEAD 8
 #endif
 
+// LDS that holds the Q^T fragments a wave parks outside its registers (one
+// object per instantiation that uses it).
+template <int BYTES>
+__device__ __forceinline__ char* q_stash() {
+    __shared__ __attribute__((aligned(1024))) char buf[BYTES];
+    return buf;
+}
+
 template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN, bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdParams p) {
@@ -45,6 +53,17 @@ void attn_fwd_kernel(FwdParams p) {
     constexpr int KB = BC / 32;  // 32-key blocks per tile
     constexpr int DB = D / 32;   // 32-wide d blocks of O^T
     constexpr int KS = D / 16;   // 16-wide d steps of S^T
+    // At d = 256 the Q^T and O^T registers of a 32-row wave (64 + 128) leave
+    // too few for two waves per SIMD, so the second half of each lane's Q^T
+    // fragments is parked in LDS and read back every tile (each lane reads
+    // only what it wrote, so no barrier is involved).
+    constexpr int KS_REG = (D == 256 && WPE >= 2) ? KS / 2 : KS;
+    constexpr int KS_LDS = KS - KS_REG;
+    // LDS reads per score MFMA group once the first ATTN_FWD_K_LEAD are out.
+    constexpr int DS_GROUPS = KS * KB > ATTN_FWD_K_LEAD ? KS * KB - ATTN_FWD_K_LEAD : 1;
+    constexpr int DS_PER = (KS * KB + KS_LDS * QB - ATTN_FWD_K_LEAD) / DS_GROUPS;
+    static_assert(KS_LDS == 0 || DS_PER * DS_GROUPS == KS * KB + KS_LDS * QB - ATTN_FWD_K_LEAD,
+                  "even LDS read schedule");
     using Tile = KVDirect<D, BC, NW>;
     // Two LDS stages as distinct objects, and a loop unrolled by two so that
     // every access names its stage statically: the compiler can then see that
@@ -188,8 +207,18 @@ void attn_fwd_kernel(FwdParams p) {
         }
     };
 
-    // Q^T fragments (B operand), resident for the whole loop.
-    u32x4 qf[QB][KS];
+    // Q^T fragments (B operand), resident for the whole loop: steps below
+    // KS_REG in registers, the rest in this wave's LDS slots (16 bytes per
+    // lane and step).
+    u32x4 qf[QB][KS_REG];
+    char* qlds = nullptr;
+    if constexpr (KS_LDS > 0) qlds = q_stash<NW * QB * KS_LDS * 1024>() + wave * (QB * KS_LDS * 1024) + lane * 16;
+    auto q_frag = [&](int qb, int s) __attribute__((always_inline)) {
+        if constexpr (KS_LDS > 0) {
+            if (s >= KS_REG) return *reinterpret_cast<const u32x4*>(qlds + (qb * KS_LDS + s - KS_REG) * 1024);
+        }
+        return qf[qb][s < KS_REG ? s : 0];
+    };
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = wr0 + 32 * qb + l32;
@@ -198,7 +227,10 @@ void attn_fwd_kernel(FwdParams p) {
         for (int s = 0; s < KS; ++s) {
             u32x4 z = {0u, 0u, 0u, 0u};
             if (row < Nq) z = load16(qrow + (2 * s + (lane >> 5)) * 8);
-            qf[qb][s] = z;
+            if (s < KS_REG)
+                qf[qb][s < KS_REG ? s : 0] = z;
+            else if constexpr (KS_LDS > 0)
+                *reinterpret_cast<u32x4*>(qlds + (qb * KS_LDS + s - KS_REG) * 1024) = z;
         }
     }
 
@@ -249,16 +281,17 @@ void attn_fwd_kernel(FwdParams p) {
                 for (int kb = 0; kb < KB; ++kb) {
                     const u32x4 a = read_k_frag<D>(ks, kb, s, lane);
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma32(a, qf[qb][s], sacc[kb][qb]);
+                    for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma32(a, q_frag(qb, s), sacc[kb][qb]);
                 }
             }
-            // Keep the K fragment reads ATTN_FWD_K_LEAD MFMAs ahead of their
-            // use so that LDS latency is not exposed before each MFMA.
+            // Keep the K (and parked Q) fragment reads ATTN_FWD_K_LEAD MFMAs
+            // ahead of their use so that LDS latency is not exposed before
+            // each MFMA.
             __builtin_amdgcn_sched_group_barrier(0x100, ATTN_FWD_K_LEAD, 0);  // DS read
 #pragma unroll
             for (int i = 0; i < KS * KB - ATTN_FWD_K_LEAD; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);       // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, DS_PER, 0);   // DS read
             }
             __builtin_amdgcn_sched_group_barrier(0x008, QB * ATTN_FWD_K_LEAD, 0);
             // ---- mask: only tiles crossing the diagonal or the key end ----
@@ -410,8 +443,11 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, boo
 #ifndef ATTN_FWD64_CFG
 #define ATTN_FWD64_CFG 1, 64, 4, 4
 #endif
+// d = 256: eight waves at two per SIMD with half of Q^T parked in LDS (64 KiB
+// of K/V stages + 64 KiB of parked Q): 930 TFLOP/s on the chunked-prefill
+// workload against 710 for four waves at one per SIMD with Q^T in registers.
 #ifndef ATTN_FWD256_CFG
-#define ATTN_FWD256_CFG 1, 32, 4, 1
+#define ATTN_FWD256_CFG 1, 32, 8, 2
 #endif
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, bool paged, hipStream_t s) {

@@ -75,6 +75,7 @@ SMALL_DENSE = [
     (1, 600, 1100, 8, 2, 128, False),
     (1, 1000, 1000, 4, 4, 128, True),
     (1, 64, 65, 4, 1, 256, True),
+    (2, 600, 700, 4, 2, 256, True),    # d = 256: three 256-row query tiles, ragged tails
 ]
 
 

@@ -76,7 +76,8 @@ def paged_prefill_case(nq, nk, hq, hkv, d, seed, poison=True):
 
 
 @pytest.mark.parametrize("d,causal,window", [(128, True, (-1, -1)), (64, True, (200, -1)),
-                                             (256, False, (-1, -1)), (128, False, (300, 10))])
+                                             (256, False, (-1, -1)), (128, False, (300, 10)),
+                                             (256, True, (-1, -1))])
 def test_paged_prefill(d, causal, window):
     nk = [300, 1, 2049, 512, 4100]
     nq = [300, 1, 17, 0, 1025]  # the new rows are the last keys of each sequence
