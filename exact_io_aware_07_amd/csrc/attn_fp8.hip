@@ -140,9 +140,13 @@ __global__ __launch_bounds__(2 * D) void attn_fp8_quant_kernel(Fp8QuantParams p)
     __shared__ __attribute__((aligned(16))) uint8_t tile[VT ? D * kFp8Block : 16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nblk = (p.n + kFp8Block - 1) / kFp8Block;
-    const int kb = blockIdx.x % nblk;
-    const int bh = blockIdx.x / nblk;
-    const int h = bh % p.heads, b = bh / p.heads;
+    // Heads fastest: the workgroups that run together read whole rows (all
+    // heads of the same 64 positions) rather than one head's 2 d bytes of
+    // many rows (2-5% faster).
+    const int h = blockIdx.x % p.heads;
+    const int kb = (blockIdx.x / p.heads) % nblk;
+    const int b = blockIdx.x / (p.heads * nblk);
+    const int bh = b * p.heads + h;
     const int j = tid & (L - 1);  // 8-value chunk of the rows
     const int r0 = 4 * (tid / L);  // first of this thread's four rows
 

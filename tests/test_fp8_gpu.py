@@ -159,3 +159,12 @@ def test_fwd_fp8_prefill_workload_sampled():
     case = W.config_case("mha_causal_b4_h16_n4096_d128", device="cpu")
     rows = [(0, 0, 0), (0, 5, 63), (1, 15, 64), (2, 7, 2047), (3, 3, 4095), (3, 15, 1000), (1, 0, 4000)]
     check_fp8(case, True, True, seed=9, rows=rows)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_fwd_fp8_head_dims_long_sampled(d):
+    """d = 64 and 256 over 2048 causal keys (many tiles and query tiles, GQA), all codes bit for bit,
+    sampled rows against the oracle."""
+    case = W.dense_case(2, 2048, 2048, 8, 2, d, seed=31 + d, k_outlier_frac=0.01)
+    rows = [(0, 0, 0), (0, 7, 255), (1, 3, 256), (1, 4, 1023), (0, 2, 2047), (1, 6, 1500), (0, 5, 777)]
+    check_fp8(case, True, True, seed=17, rows=rows)
