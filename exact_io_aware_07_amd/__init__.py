@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "AttnError", "lib", "lib_path", "attn_fwd", "attn_fwd_paged", "attn_bwd", "attn_bwd_workspace_bytes",
     "attn_decode_splitkv", "attn_decode_combine",
-    "attn_decode", "attn_decode_num_splits", "attn_decode_default_chunk",
+    "attn_decode", "attn_decode_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES", "attn_decode_num_splits", "attn_decode_default_chunk",
     "attn_decode_workspace_bytes", "attn_check_cu_seqlens", "attn_check_block_table",
     "STATUS",
 ]
@@ -51,6 +51,7 @@ _SIGNATURES = {
     "attn_bwd_workspace_bytes": ([_I, _I], ctypes.c_size_t),
     "attn_decode_splitkv": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "attn_decode_combine": ([_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "attn_decode_noalloc": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "attn_decode_kvcache": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                              _I, _I, _I, _F, _P, _P, _P, _P, _P, _P], _I),
     "attn_fp8_quantize": ([_P, _P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
@@ -70,6 +71,9 @@ _SIGNATURES = {
 }
 
 _lib = None
+
+# ATTN_DECODE_NOALLOC_SCRATCH_BYTES of include/attn.h.
+DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class AttnError(RuntimeError):
@@ -390,6 +394,44 @@ def attn_decode(q, k_cache, v_cache, block_table, seqlens_k, *, max_seqlen_k, so
                                  chunk_tokens=chunk_tokens, num_splits=n,
                                  softmax_scale=softmax_scale, stream=stream)
     return attn_decode_combine(po, pl, seqlens_k, chunk_tokens=chunk_tokens, stream=stream)
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, block_table, seqlens_k, *, max_seqlen_k, softmax_scale,
+                        chunk_tokens=None, out=None, lse=None, return_lse=True, stream=None):
+    """Split + combine with the partials in the library's own device array: the C call
+    allocates nothing (pass `out` and `lse` to allocate nothing here either)."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(seqlens_k, "seqlens_k", torch.int32, dev)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expects q [B,Hq,d] and caches [P,page,Hkv,d]")
+    batch, hq, d = q.shape
+    num_pages, page, hkv, dk = k_cache.shape
+    if dk != d or block_table.dim() != 2 or block_table.shape[0] != batch or seqlens_k.shape != (batch,):
+        raise ValueError("inconsistent decode shapes")
+    if chunk_tokens is None:
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        chunk_tokens = attn_decode_default_chunk(batch, hkv, max_seqlen_k, cus)
+    n = max(1, attn_decode_num_splits(max_seqlen_k, chunk_tokens))
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    if return_lse and lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    if lse is not None:
+        _need(lse, "lse", torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = lib().attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(seqlens_k), batch, hq, hkv, d, page, block_table.shape[1],
+                                       num_pages, int(chunk_tokens), n, float(softmax_scale), _ptr(out),
+                                       _ptr(lse), _stream(stream, dev))
+    _check(st)
+    return out, lse
 
 
 def attn_decode_kvcache(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_k, *, max_seqlen_k,

@@ -11,6 +11,14 @@
 #include "attn_launch.h"
 
 #include <algorithm>
+#include <mutex>
+
+// Partials of attn_decode_noalloc: a file-scope device array, so that the
+// call needs no allocation.  Each GPU the library runs on holds its own copy
+// (ATTN_DECODE_NOALLOC_SCRATCH_BYTES) until the process ends.  Host code never
+// passes this name to a kernel: its device address comes from
+// hipGetSymbolAddress, once per device (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -60,6 +68,30 @@ attn_status_t check_scale(float s) {
 attn_status_t hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept for later calls.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+attn_status_t scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_HIP, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || addr == nullptr)
+            return fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = addr;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ATTN_OK;
 }
 
 }  // namespace
@@ -339,6 +371,40 @@ attn_status_t attn_decode_combine(const float* out_partial, const float* lse_par
     p.n_splits = num_splits;
     return hip_status(attn::launch_decode_combine(p, head_dim, static_cast<hipStream_t>(stream)),
                       "attn_decode_combine launch");
+}
+
+attn_status_t attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seqlens_k, int batch,
+                                  int num_heads_q, int num_heads_kv, int head_dim, int page_size,
+                                  int max_pages_per_seq, int num_pages, int chunk_tokens,
+                                  int num_splits, float softmax_scale, void* out, float* lse,
+                                  void* stream) {
+    // Host-only checks first (no HIP call before the sizes are known to fit).
+    if (!out) return fail(ATTN_ERR_NULL, "out must be non-NULL");
+    if (misaligned(16, out) || misaligned(4, lse)) return fail_align();
+    if (batch < 1 || num_heads_q < 1 || num_splits < 1 || !head_dim_supported(head_dim))
+        return fail(batch < 1 || num_heads_q < 1 || num_splits < 1 ? ATTN_ERR_SHAPE : ATTN_ERR_UNSUPPORTED,
+                    "batch=%d num_heads_q=%d num_splits=%d head_dim=%d", batch, num_heads_q, num_splits,
+                    head_dim);
+    const size_t obytes = (size_t)num_splits * batch * num_heads_q * head_dim * 4;
+    const size_t need = attn_decode_workspace_bytes(batch, num_heads_q, head_dim, num_splits);
+    if (need > (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_SHAPE, "partials need %zu bytes, more than the %zu-byte scratch of "
+                    "attn_decode_noalloc (use attn_decode_splitkv with a workspace)", need,
+                    (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
+    void* base = nullptr;
+    attn_status_t st = scratch_on_current_device(&base);
+    if (st != ATTN_OK) return st;
+    float* out_partial = static_cast<float*>(base);
+    float* lse_partial = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + obytes);
+    // The split validates every remaining argument before it launches; the
+    // combine's checks are covered by those above, so only its launch can fail.
+    st = attn_decode_splitkv(q, k_cache, v_cache, block_table, seqlens_k, batch, num_heads_q,
+                             num_heads_kv, head_dim, page_size, max_pages_per_seq, num_pages,
+                             chunk_tokens, num_splits, softmax_scale, out_partial, lse_partial, stream);
+    if (st != ATTN_OK) return st;
+    return attn_decode_combine(out_partial, lse_partial, seqlens_k, batch, num_heads_q, head_dim,
+                               chunk_tokens, num_splits, out, lse, stream);
 }
 
 attn_status_t attn_decode_kvcache(const void* q, const void* k_new, const void* v_new, void* k_cache,

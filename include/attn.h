@@ -310,6 +310,34 @@ attn_status_t attn_decode_combine(const float* out_partial, const float* lse_par
                                   void* out, float* lse, void* stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode_splitkv followed by attn_decode_combine,
+ * with the partials kept in a device array inside the library instead of a
+ * caller workspace.  For callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the call allocates and frees nothing.
+ *
+ * Arguments are those of attn_decode_splitkv without out_partial and
+ * lse_partial, plus out and lse as in attn_decode_combine.  The partials
+ * (attn_decode_workspace_bytes(batch, num_heads_q, head_dim, num_splits)
+ * bytes) must fit in ATTN_DECODE_NOALLOC_SCRATCH_BYTES, else ATTN_ERR_SHAPE
+ * is returned before any HIP call.  The array is per GPU (the current
+ * device; `stream` must belong to it), is held from the first call on that
+ * GPU until the process ends, and is shared by every call on that GPU: calls
+ * on one stream are ordered, calls that overlap on different streams of the
+ * same GPU race and give undefined results.  Every partial the combine reads
+ * is written by the split of the same call, so nothing needs clearing.
+ * Errors in the arguments are returned before anything is enqueued; a failed
+ * combine launch can leave the split enqueued.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+attn_status_t attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seqlens_k,
+                                  int batch, int num_heads_q, int num_heads_kv, int head_dim,
+                                  int page_size, int max_pages_per_seq, int num_pages,
+                                  int chunk_tokens, int num_splits, float softmax_scale,
+                                  void* out, float* lse, void* stream);
+
+/*
  * attn_decode_kvcache -- one decode step that first appends the new token to
  * the paged cache in place, with optional rotary embedding, then decodes over
  * the cache including it ("Deep Dive - FlashAttention", "Paged KV is a

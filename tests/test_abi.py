@@ -322,3 +322,43 @@ def test_ceiling_mfma_rejects(fn, kw, code):
     a = dict(ops=FAKE, waves=8, iters=10, sink=OUT)
     a.update(kw)
     assert getattr(ea.lib(), fn)(a["ops"], a["waves"], a["iters"], a["sink"], None) == code
+
+
+def dec_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE2, vc=FAKE3, bt=ctypes.c_void_p(0x60000), sl=ctypes.c_void_p(0x70000),
+             batch=2, hq=8, hkv=2, d=128, page=256, maxp=4, npages=8, chunk=512, nsplit=2,
+             scale=0.1, out=OUT, lse=LSE)
+    a.update(kw)
+    return ea.lib().attn_decode_noalloc(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["batch"], a["hq"],
+                                        a["hkv"], a["d"], a["page"], a["maxp"], a["npages"], a["chunk"],
+                                        a["nsplit"], a["scale"], a["out"], a["lse"], None)
+
+
+# Only checks that fail before the scratch address is looked up (no HIP call).
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=NULL), 1), (dict(batch=0), 2), (dict(hq=0), 2), (dict(nsplit=0), 2), (dict(d=96), 3),
+    (dict(out=ctypes.c_void_p(0x40000000 + 8)), 3), (dict(lse=ctypes.c_void_p(0x50000000 + 2)), 3),
+])
+def test_decode_noalloc_rejects(kw, code):
+    assert dec_noalloc(**kw) == code
+    assert ea.lib().attn_last_error().decode()
+
+
+def test_decode_noalloc_rejects_partials_beyond_scratch():
+    """Partials larger than the library's array are refused with a clear message."""
+    lib = ea.lib()
+    limit = ea.DECODE_NOALLOC_SCRATCH_BYTES
+    # 64 requests x 32 heads x d=128: one split needs 64*32*129*4 = 1,056,768 bytes.
+    per_split = lib.attn_decode_workspace_bytes(64, 32, 128, 1)
+    fits = limit // per_split
+    too_many = fits + 1
+    assert lib.attn_decode_workspace_bytes(64, 32, 128, too_many) > limit
+    assert dec_noalloc(batch=64, hq=32, hkv=8, nsplit=too_many) == 2
+    msg = lib.attn_last_error().decode()
+    assert "scratch" in msg and str(limit) in msg
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    m = re.search(r"#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ea.DECODE_NOALLOC_SCRATCH_BYTES
