@@ -10,10 +10,16 @@ Each kernel is bracketed by HIP events recorded on the stream it is launched
 on (torch's current stream).  The headline value is the prefill throughput in
 TFLOP/s (4*Nq*Nk*d per head, halved for causal); the decode leg reports HBM
 GB/s over its algorithmic bytes (K/V rows used, q, out, lse, block table and
-lengths).  The CPU oracle is timed on a bounded sample of the prefill
-workload as a reported baseline.
+lengths).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+Every other workload is timed as a leg of its own after the step (per-launch
+mean, p50 and p95, roofline against the published peak, counter traffic):
+the non-causal d=64 case, the causal GQA N=8192 case with key outliers, the
+packed chunked prefill at d = 128, 64 and 256, and the widened rows (backward,
+decode with append + rotary, FP8 forward).  The CPU oracle is timed on a
+bounded sample of every workload as a reported baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--legs step,c1,...]
 """
 import argparse
 import hashlib
@@ -30,6 +36,11 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PREFILL = "mha_causal_b4_h16_n4096_d128"
 DECODE = "paged_decode_b64_hq32_hkv8_d128"
+NONCAUSAL = "mha_noncausal_b1_h4_n512_d64"
+GQA = "gqa_causal_b2_hq32_hkv8_n8192_d128_koutliers"
+VARLEN = "varlen_chunked_prefill_16seq_hq32_hkv8"
+# Legs: the step (prefill + decode, the headline) and the separately timed ones.
+LEGS = ["step", "c1", "c3", "c4_d128", "c4_d64", "c4_d256", "backward", "kvcache", "fp8", "ceilings"]
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = ["attn_tile.h", "attn_launch.h", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_fp8.hip"]
 
@@ -77,8 +88,9 @@ def decode_bytes(case):
     return kv + qo + lse + table
 
 
-def load_traffic(kernel_key, digest):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if current."""
+def load_traffic(leg, kernel_key, digest):
+    """HBM bytes per launch of one kernel of one leg, from the committed
+    rocprofv3 counter runs of that leg, if they match the current sources."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
@@ -86,19 +98,20 @@ def load_traffic(kernel_key, digest):
         return None
     if rec.get("source_digest") != digest:
         return None
-    k = rec.get("kernels", {}).get(kernel_key)
+    k = rec.get("legs", {}).get(leg, {}).get("kernels", {}).get(kernel_key)
     if not k:
         return None
     return k.get("hbm_bytes_per_launch")
 
 
 # Counter key -> substring of the rocprofv3 kernel name ("<" keeps attn_fwd_kernel
-# apart from attn_fwd_fp8_kernel).  Per-launch figures average every dispatch
-# of the run, so a kernel shared by two legs (the decode split kernel) averages
-# over both.
+# apart from attn_fwd_fp8_kernel).  Each leg is profiled in a run of its own
+# (bench.py --legs LEG), so per-launch figures average only that leg's
+# dispatches.
 TRAFFIC_KERNELS = {
     "attn_fwd_kernel": "attn_fwd_kernel<",
     "attn_decode_split_kernel": "attn_decode_split_kernel<",
+    "attn_decode_combine_kernel": "attn_decode_combine_kernel<",
     "attn_decode_append_kernel": "attn_decode_append_kernel<",
     "attn_bwd_dkdv": "attn_bwd_dkdv_",  # attn_bwd_dkdv_kernel (d = 64) or attn_bwd_dkdv_pair_kernel (d = 128)
     "attn_bwd_dq_kernel": "attn_bwd_dq_kernel<",
@@ -107,9 +120,9 @@ TRAFFIC_KERNELS = {
 }
 
 
-def traffic_sum(keys, digest):
-    """Sum of the per-launch HBM bytes of several kernels, or None if any is missing."""
-    vals = [load_traffic(k, digest) for k in keys]
+def traffic_sum(leg, keys, digest):
+    """Sum of the per-launch HBM bytes of several kernels of a leg, or None if any is missing."""
+    vals = [load_traffic(leg, k, digest) for k in keys]
     return None if any(v is None for v in vals) else sum(vals)
 
 
@@ -125,18 +138,27 @@ def _counter_rows(path, counter):
     return rows
 
 
-def write_traffic(fetch_csv, write_csv, copy_mib, commands):
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch)
-    of `bench.py --copy-calibration-mib N` into profiles/hbm_traffic.json.
+def write_traffic(runs, copy_mib, commands):
+    """Merge rocprofv3 --pmc runs into profiles/hbm_traffic.json.
 
-    The calibration copy (a same-dtype tensor copy, which the HIP runtime runs
-    as its copyBuffer blit kernel) reads and writes N MiB exactly once; the
-    ratio of that size to what each counter reports for it scales the counter
-    for the attention kernels.  It is the copyBuffer dispatch with the largest
-    counter value.
+    runs: (leg, fetch_csv, write_csv) per leg, each pair from two runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of `bench.py --legs LEG
+    --copy-calibration-mib N`.  The calibration copy (a same-dtype tensor
+    copy, which the HIP runtime runs as its copyBuffer blit kernel) reads and
+    writes N MiB exactly once; the ratio of that size to what each counter
+    reports for it scales the counter for the attention kernels of the same
+    run.  It is the copyBuffer dispatch with the largest counter value.
     """
-    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
-    write = _counter_rows(write_csv, "WRITE_SIZE")
+    digest = source_digest()
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+        if rec.get("source_digest") != digest or "legs" not in rec:
+            rec = None
+    except (OSError, ValueError):
+        rec = None
+    if rec is None:
+        rec = {"source_digest": digest, "legs": {}}
     expect_kib = copy_mib * 1024.0
 
     def calib(rows):
@@ -146,29 +168,31 @@ def write_traffic(fetch_csv, write_csv, copy_mib, commands):
         measured = max(copies)
         return expect_kib / measured, measured
 
-    fr, fm = calib(fetch)
-    wr, wm = calib(write)
-    kernels = {}
-    for key, pat in TRAFFIC_KERNELS.items():
-        fv = [v for n, v in fetch if pat in n]
-        wv = [v for n, v in write if pat in n]
-        if not fv or not wv:
-            continue
-        f_kib = sum(fv) / len(fv)
-        w_kib = sum(wv) / len(wv)
-        kernels[key] = {
-            "dispatches": [len(fv), len(wv)],
-            "fetch_kib_per_launch": round(f_kib, 1),
-            "write_kib_per_launch": round(w_kib, 1),
-            "hbm_bytes_per_launch": int(round((f_kib * fr + w_kib * wr) * 1024)),
+    for leg, fetch_csv, write_csv in runs:
+        fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+        write = _counter_rows(write_csv, "WRITE_SIZE")
+        fr, fm = calib(fetch)
+        wr, wm = calib(write)
+        kernels = {}
+        for key, pat in TRAFFIC_KERNELS.items():
+            fv = [v for n, v in fetch if pat in n]
+            wv = [v for n, v in write if pat in n]
+            if not fv or not wv:
+                continue
+            f_kib = sum(fv) / len(fv)
+            w_kib = sum(wv) / len(wv)
+            kernels[key] = {
+                "dispatches": [len(fv), len(wv)],
+                "fetch_kib_per_launch": round(f_kib, 1),
+                "write_kib_per_launch": round(w_kib, 1),
+                "hbm_bytes_per_launch": int(round((f_kib * fr + w_kib * wr) * 1024)),
+            }
+        rec["legs"][leg] = {
+            "commands": [c for c in commands if f"--legs {leg} " in c + " "],
+            "copy_calibration": {"mib": copy_mib, "fetch_kib_measured": fm, "write_kib_measured": wm,
+                                 "fetch_scale": round(fr, 4), "write_scale": round(wr, 4)},
+            "kernels": kernels,
         }
-    rec = {
-        "source_digest": source_digest(),
-        "commands": commands,
-        "copy_calibration": {"mib": copy_mib, "fetch_kib_measured": fm, "write_kib_measured": wm,
-                             "fetch_scale": round(fr, 4), "write_scale": round(wr, 4)},
-        "kernels": kernels,
-    }
     with open(PROFILE_TRAFFIC, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -209,7 +233,7 @@ def time_backward(ea, pc, out, lse, stream, torch, digest, reps=10):
             "algorithmic_bytes": alg,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": traffic_sum(["attn_bwd_dkdv", "attn_bwd_dq_kernel"], digest)},
+                         "traffic": traffic_sum("backward", ["attn_bwd_dkdv", "attn_bwd_dq_kernel"], digest)},
             "workload": PREFILL}
 
 
@@ -265,7 +289,7 @@ def time_decode_kvcache(ea, W, dev, props, stream, torch, digest, reps=20):
             "algorithmic_bytes": nbytes, "chunk_tokens": chunk, "splits": n,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_sum(["attn_decode_append_kernel", "attn_decode_split_kernel"], digest)},
+                         "traffic": traffic_sum("kvcache", ["attn_decode_append_kernel", "attn_decode_split_kernel"], digest)},
             "workload": DECODE + " with one appended token per request, rotary over all 128 features"}
 
 
@@ -317,7 +341,7 @@ def time_fp8(ea, W, pc, stream, torch, digest, reps=20):
             "algorithmic_bytes": alg,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                         "traffic": load_traffic("attn_fwd_fp8_kernel", digest)},
+                         "traffic": load_traffic("fp8", "attn_fwd_fp8_kernel", digest)},
             "quantize_ms_mean": round(q_ms, 4), "quantize_gbs": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
             "end_to_end_tflops": round(flops / ((q_ms + a_ms) * 1e-3) / 1e12, 2),
             "workload": PREFILL + ", E4M3, 64-row block scales, Q and K turned by a random-sign Hadamard transform"}
@@ -367,8 +391,33 @@ def add_measured(roof, ceiling):
         roof["frac_measured"] = round(roof["achieved"] / ceiling, 4)
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """The fp64 oracle on whole (batch, head) pairs of the prefill workload."""
+def _cpu_info():
+    """(BLAS/OpenMP threads the oracle runs with, CPU model)."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return threads, cpu
+
+
+def _cpu_record(value, unit, sample):
+    threads, cpu = _cpu_info()
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "sample": sample,
+            "cpu": cpu, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline_dense(case, name, budget_s):
+    """The fp64 oracle on whole (batch, head) pairs of a dense workload, until
+    the time budget is spent; metric FLOPs of the pairs done / time."""
     import numpy as np
     import torch
 
@@ -390,30 +439,141 @@ def cpu_baseline(case, budget_s=12.0):
             break
     elapsed = time.perf_counter() - t0
     per_head = prefill_flops(case) / (B * Hq)
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001 - threadpoolctl is optional
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    cpu = "unknown"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
+    masked = " (materialising S, masked half included)" if case["causal"] else " (materialising S)"
+    return _cpu_record(per_head * done / elapsed / 1e12, "TFLOP/s",
+                       f"{done} of {B * Hq} (batch, head) pairs of {name}, each the full "
+                       f"{case['Nq']}x{case['Nk']} problem in fp64 NumPy{masked}, {elapsed:.1f} s; "
+                       f"metric FLOPs as on the GPU")
+
+
+def cpu_baseline_varlen(case, name, budget_s):
+    """The fp64 oracle on whole (sequence, head) pairs of the packed workload,
+    longest sequences first, until the time budget is spent."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    q, k, v = (case[x].to("cpu", dtype=torch.float32).numpy() for x in "qkv")
+    cq, ck = case["cu_seqlens_q"].tolist(), case["cu_seqlens_k"].tolist()
+    Hq, g = case["Hq"], case["Hq"] // case["Hkv"]
+    order = sorted(range(len(case["nq"])), key=lambda s: -case["nk"][s])
+    flops = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    for s in order:
+        for h in range(Hq):
+            nq, nk = case["nq"][s], case["nk"][s]
+            oracle.attention_ref(q[None, cq[s]:cq[s + 1], h:h + 1].astype(np.float64),
+                                 k[None, ck[s]:ck[s + 1], h // g:h // g + 1].astype(np.float64),
+                                 v[None, ck[s]:ck[s + 1], h // g:h // g + 1].astype(np.float64),
+                                 causal=True, softmax_scale=case["scale"])
+            flops += 4.0 * nq * nk * case["d"] / 2
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
                 break
-    except OSError:
-        pass
-    return {
-        "value": per_head * done / elapsed / 1e12,
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": (f"{done} of {B * Hq} (batch, head) pairs of {PREFILL}, each the full "
-                   f"{case['Nq']}x{case['Nk']} causal problem in fp64 NumPy (materialising S, "
-                   f"masked half included), {elapsed:.1f} s; metric FLOPs as on the GPU"),
-        "cpu": cpu,
-        "affinity_cpus": len(os.sched_getaffinity(0)),
-    }
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    elapsed = time.perf_counter() - t0
+    return _cpu_record(flops / elapsed / 1e12, "TFLOP/s",
+                       f"{done} of {len(order) * Hq} (sequence, head) pairs of {name} at d={case['d']}, "
+                       f"longest sequences first, in fp64 NumPy (materialising S), {elapsed:.1f} s; "
+                       f"metric FLOPs (halved for causal) as on the GPU")
+
+
+def cpu_baseline_decode(case, budget_s):
+    """The fp64 decode oracle (gather, then the definition, unsplit) on whole
+    requests until the time budget is spent; algorithmic bytes / time.  Each
+    request's pages are copied out of the cache before its timed call."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    lens = case["seqlens_k"].tolist()
+    page = case["page"]
+    table = case["block_table"].to("cpu")
+    nbytes = 0
+    done = 0
+    elapsed = 0.0
+    for b in range(case["B"]):
+        n_pages = -(-lens[b] // page)
+        idx = table[b, :n_pages].to(case["k_cache"].device, torch.long)
+        kc = case["k_cache"].index_select(0, idx).to("cpu", torch.float32).numpy()
+        vc = case["v_cache"].index_select(0, idx).to("cpu", torch.float32).numpy()
+        q = case["q"][b:b + 1].to("cpu", torch.float32).numpy()
+        t0 = time.perf_counter()
+        oracle.decode_ref(q.astype(np.float64), kc, vc, np.arange(n_pages)[None], [lens[b]],
+                          softmax_scale=case["scale"])
+        elapsed += time.perf_counter() - t0
+        nbytes += (lens[b] * case["Hkv"] * case["d"] * 4 + 2 * case["Hq"] * case["d"] * 2 + 4 * case["Hq"]
+                   + 4 * n_pages + 4)
+        done += 1
+        if elapsed >= budget_s:
+            break
+    return _cpu_record(nbytes / elapsed / 1e9, "GB/s",
+                       f"{done} of {case['B']} requests of {DECODE} (each over all its cached keys, "
+                       f"{sum(lens[:done])} keys in all) in fp64 NumPy, {elapsed:.1f} s of oracle time; "
+                       f"the request's algorithmic bytes as on the GPU")
+
+
+def varlen_flops(case):
+    """Metric FLOPs of a packed causal batch: 4*Nq*Nk*d per (sequence, head), halved."""
+    return sum(4.0 * nq * nk * case["d"] / 2 for nq, nk in zip(case["nq"], case["nk"])) * case["Hq"]
+
+
+def varlen_flops_exact(case):
+    """4*d per allowed (query, key) pair, bottom-right causal per sequence."""
+    pairs = 0
+    for nq, nk in zip(case["nq"], case["nk"]):
+        pairs += sum(max(0, min(nk, i + nk - nq + 1)) for i in range(nq))
+    return 4.0 * case["d"] * pairs * case["Hq"]
+
+
+def varlen_bytes(case):
+    """Compulsory traffic of a packed batch: Q, K, V read once, out and lse written once."""
+    tq, tk = sum(case["nq"]), sum(case["nk"])
+    return 2 * (2 * tq * case["Hq"] * case["d"] + 2 * tk * case["Hkv"] * case["d"]) + 4 * case["Hq"] * tq
+
+
+def time_launches(fn, stream, torch, reps, warm=3):
+    """Per-launch times (ms) of fn, each bracketed by events on `stream`."""
+    for _ in range(warm):
+        fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return [e[0].elapsed_time(e[1]) for e in ev]
+
+
+def _stats(ms):
+    mean = sum(ms) / len(ms)
+    srt = sorted(ms)
+    pct = lambda p: srt[min(len(srt) - 1, int(round(p * (len(srt) - 1))))]
+    return mean, pct(0.5), pct(0.95)
+
+
+def fwd_leg(ea, case, workload, leg, stream, torch, digest, flops, flops_exact, nbytes, reps=20):
+    """One attn_fwd workload timed on its own: per-launch mean, p50, p95."""
+    kw = dict(causal=case["causal"], softmax_scale=case["scale"], stream=stream)
+    if "cu_seqlens_q" in case:
+        kw.update(cu_seqlens_q=case["cu_seqlens_q"], cu_seqlens_k=case["cu_seqlens_k"],
+                  max_seqlen_q=case["max_seqlen_q"], max_seqlen_k=case["max_seqlen_k"])
+    out, lse = ea.attn_fwd(case["q"], case["k"], case["v"], **kw)
+    ms = time_launches(lambda: ea.attn_fwd(case["q"], case["k"], case["v"], out=out, lse=lse, **kw),
+                       stream, torch, reps)
+    mean, p50, p95 = _stats(ms)
+    tf = flops / (mean * 1e-3) / 1e12
+    return {"workload": workload, "kernel_ms_mean": round(mean, 4), "kernel_ms_p50": round(p50, 4),
+            "kernel_ms_p95": round(p95, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+            "flops_metric": flops, "flops_exact": flops_exact,
+            "tflops_exact": round(flops_exact / (mean * 1e-3) / 1e12, 2), "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic(leg, "attn_fwd_kernel", digest)}}
 
 
 def main():
@@ -421,31 +581,25 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help=f"comma-separated legs to run (default: all of {','.join(LEGS)}); "
+                         "the headline value needs 'step'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-backward", action="store_true",
-                    help="skip the separately timed attn_bwd leg (not part of the step)")
-    ap.add_argument("--no-kvcache", action="store_true",
-                    help="skip the separately timed attn_decode_kvcache leg (not part of the step)")
-    ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the separately timed FP8 forward leg (not part of the step)")
-    ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip measuring the HBM-read and matrix-core ceilings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for counter scaling)")
-    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="CPU only: write profiles/hbm_traffic.json from two rocprofv3 --pmc "
-                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) of a run with "
-                         "--copy-calibration-mib, then exit")
+    ap.add_argument("--write-traffic", nargs=3, action="append", metavar=("LEG", "FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: merge two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a `--legs LEG --copy-calibration-mib N` run into "
+                         "profiles/hbm_traffic.json (repeatable), then exit")
     ap.add_argument("--traffic-commands", nargs="*", default=[],
                     help="with --write-traffic: the profiler commands, stored with the figures")
     args = ap.parse_args()
     if args.write_traffic:
         if not args.copy_calibration_mib:
-            print("--write-traffic needs the --copy-calibration-mib value of the profiled run",
+            print("--write-traffic needs the --copy-calibration-mib value of the profiled runs",
                   file=sys.stderr)
             return 2
-        return write_traffic(args.write_traffic[0], args.write_traffic[1],
-                             args.copy_calibration_mib, args.traffic_commands)
+        return write_traffic(args.write_traffic, args.copy_calibration_mib, args.traffic_commands)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -454,6 +608,12 @@ def main():
     if args.steps < 1:
         print("--steps must be >= 1", file=sys.stderr)
         return 2
+    legs = [x for x in args.legs.split(",") if x]
+    unknown = [x for x in legs if x not in LEGS]
+    if unknown:
+        print(f"unknown legs {unknown}; choose from {LEGS}", file=sys.stderr)
+        return 2
+    cpu = not args.no_cpu_baseline
 
     import torch
 
@@ -463,40 +623,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
-
-    pc = W.config_case(PREFILL, device=dev)
-    out = torch.empty_like(pc["q"])
-    lse = torch.empty((pc["B"], pc["Hq"], pc["Nq"]), dtype=torch.float32, device=dev)
-
-    dc = W.config_case(DECODE, device=dev)
-    dc_dev = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in dc.items()}
-    max_len = int(dc["seqlens_k"].max())
-    chunk = ea.attn_decode_default_chunk(dc["B"], dc["Hkv"], max_len, props.multi_processor_count)
-    n_splits = ea.attn_decode_num_splits(max_len, chunk)
-    part_o = torch.empty((n_splits, dc["B"], dc["Hq"], dc["d"]), dtype=torch.float32, device=dev)
-    part_l = torch.empty((n_splits, dc["B"], dc["Hq"]), dtype=torch.float32, device=dev)
-    dout = torch.empty((dc["B"], dc["Hq"], dc["d"]), dtype=torch.bfloat16, device=dev)
-    dlse = torch.empty((dc["B"], dc["Hq"]), dtype=torch.float32, device=dev)
-
     stream = torch.cuda.current_stream(dev)
-
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        ea.attn_fwd(pc["q"], pc["k"], pc["v"], causal=pc["causal"], softmax_scale=pc["scale"],
-                    out=out, lse=lse, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        ea.attn_decode_splitkv(dc_dev["q"], dc_dev["k_cache"], dc_dev["v_cache"],
-                               dc_dev["block_table"], dc_dev["seqlens_k"], chunk_tokens=chunk,
-                               num_splits=n_splits, softmax_scale=dc["scale"], out_partial=part_o,
-                               lse_partial=part_l, stream=stream)
-        if ev:
-            ev[2].record(stream)
-        ea.attn_decode_combine(part_o, part_l, dc_dev["seqlens_k"], chunk_tokens=chunk, out=dout,
-                               lse=dlse, stream=stream)
-        if ev:
-            ev[3].record(stream)
+    digest = source_digest()
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -507,78 +635,159 @@ def main():
         print(f"copy calibration: {n * 4} bytes read and written", file=sys.stderr, flush=True)
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    digest = source_digest()
-    bwd = None if args.no_backward else time_backward(ea, pc, out, lse, stream, torch, digest)
-    kvc = None if args.no_kvcache else time_decode_kvcache(ea, W, dev, props, stream, torch, digest)
-    fp8 = None if args.no_fp8 else time_fp8(ea, W, pc, stream, torch, digest)
-    ceil = None if args.no_ceilings else measure_ceilings(ea, torch, dev, stream)
-    pre = [e[0].elapsed_time(e[1]) for e in events]
-    spl = [e[1].elapsed_time(e[2]) for e in events]
-    cmb = [e[2].elapsed_time(e[3]) for e in events]
-    mean = lambda xs: sum(xs) / len(xs)
-    pct = lambda xs, p: sorted(xs)[min(len(xs) - 1, int(round(p * (len(xs) - 1))))]
-    pre_ms, spl_ms, cmb_ms = mean(pre), mean(spl), mean(cmb)
-
-    flops = prefill_flops(pc)
-    tflops = flops / (pre_ms * 1e-3) / 1e12
-    dbytes = decode_bytes(dc)
-    split_gbs = dbytes / (spl_ms * 1e-3) / 1e9
-    decode_gbs = dbytes / ((spl_ms + cmb_ms) * 1e-3) / 1e9
-    pre_traffic = load_traffic("attn_fwd_kernel", digest)
-    dec_traffic = load_traffic("attn_decode_split_kernel", digest)
-
     rec = {
         "metric": "attn fwd TFLOP/s (bf16 d=128 causal, % MFMA peak); decode HBM GB/s",
-        "value": round(tflops, 2),
+        "value": None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": PREFILL, "B": pc["B"], "Hq": pc["Hq"], "Hkv": pc["Hkv"],
-                   "Nq": pc["Nq"], "Nk": pc["Nk"], "d": pc["d"], "causal": pc["causal"],
-                   "decode_workload": DECODE, "decode_chunk_tokens": chunk,
-                   "decode_splits": n_splits},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": pre_traffic},
-        "prefill": {"kernel_ms_mean": round(pre_ms, 4), "kernel_ms_p50": round(pct(pre, 0.5), 4),
-                    "kernel_ms_p95": round(pct(pre, 0.95), 4), "flops_metric": flops,
-                    "flops_exact": prefill_flops_exact(pc),
-                    "tflops_exact": round(prefill_flops_exact(pc) / (pre_ms * 1e-3) / 1e12, 2),
-                    "algorithmic_bytes": prefill_bytes(pc)},
-        "decode": {"value": round(decode_gbs, 1), "unit": "GB/s",
-                   "split_ms_mean": round(spl_ms, 4), "combine_ms_mean": round(cmb_ms, 4),
-                   "split_ms_p95": round(pct(spl, 0.95), 4),
-                   "algorithmic_bytes": dbytes,
-                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1),
-                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": dec_traffic}},
-        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
-                   "cus": props.multi_processor_count, "torch": torch.__version__,
-                   "hip": getattr(torch.version, "hip", None)},
-        "kernel_source_digest": digest,
+        "config": {"workload": PREFILL},
     }
+    pc = None
+    if "step" in legs or "backward" in legs or "fp8" in legs:
+        pc = W.config_case(PREFILL, device=dev)
+        out = torch.empty_like(pc["q"])
+        lse = torch.empty((pc["B"], pc["Hq"], pc["Nq"]), dtype=torch.float32, device=dev)
+        ea.attn_fwd(pc["q"], pc["k"], pc["v"], causal=pc["causal"], softmax_scale=pc["scale"],
+                    out=out, lse=lse, stream=stream)
+
+    if "step" in legs:
+        dc = W.config_case(DECODE, device=dev)
+        dc_dev = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in dc.items()}
+        max_len = int(dc["seqlens_k"].max())
+        chunk = ea.attn_decode_default_chunk(dc["B"], dc["Hkv"], max_len, props.multi_processor_count)
+        n_splits = ea.attn_decode_num_splits(max_len, chunk)
+        part_o = torch.empty((n_splits, dc["B"], dc["Hq"], dc["d"]), dtype=torch.float32, device=dev)
+        part_l = torch.empty((n_splits, dc["B"], dc["Hq"]), dtype=torch.float32, device=dev)
+        dout = torch.empty((dc["B"], dc["Hq"], dc["d"]), dtype=torch.bfloat16, device=dev)
+        dlse = torch.empty((dc["B"], dc["Hq"]), dtype=torch.float32, device=dev)
+
+        def step(ev=None):
+            if ev:
+                ev[0].record(stream)
+            ea.attn_fwd(pc["q"], pc["k"], pc["v"], causal=pc["causal"], softmax_scale=pc["scale"],
+                        out=out, lse=lse, stream=stream)
+            if ev:
+                ev[1].record(stream)
+            ea.attn_decode_splitkv(dc_dev["q"], dc_dev["k_cache"], dc_dev["v_cache"],
+                                   dc_dev["block_table"], dc_dev["seqlens_k"], chunk_tokens=chunk,
+                                   num_splits=n_splits, softmax_scale=dc["scale"], out_partial=part_o,
+                                   lse_partial=part_l, stream=stream)
+            if ev:
+                ev[2].record(stream)
+            ea.attn_decode_combine(part_o, part_l, dc_dev["seqlens_k"], chunk_tokens=chunk, out=dout,
+                                   lse=dlse, stream=stream)
+            if ev:
+                ev[3].record(stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        pre = [e[0].elapsed_time(e[1]) for e in events]
+        spl = [e[1].elapsed_time(e[2]) for e in events]
+        cmb = [e[2].elapsed_time(e[3]) for e in events]
+        pre_ms, pre_p50, pre_p95 = _stats(pre)
+        spl_ms, _, spl_p95 = _stats(spl)
+        cmb_ms = sum(cmb) / len(cmb)
+        flops = prefill_flops(pc)
+        tflops = flops / (pre_ms * 1e-3) / 1e12
+        dbytes = decode_bytes(dc)
+        split_gbs = dbytes / (spl_ms * 1e-3) / 1e9
+        decode_gbs = dbytes / ((spl_ms + cmb_ms) * 1e-3) / 1e9
+        rec.update({
+            "value": round(tflops, 2),
+            "ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "config": {"workload": PREFILL, "B": pc["B"], "Hq": pc["Hq"], "Hkv": pc["Hkv"],
+                       "Nq": pc["Nq"], "Nk": pc["Nk"], "d": pc["d"], "causal": pc["causal"],
+                       "decode_workload": DECODE, "decode_chunk_tokens": chunk,
+                       "decode_splits": n_splits},
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic("step", "attn_fwd_kernel", digest)},
+            "prefill": {"kernel_ms_mean": round(pre_ms, 4), "kernel_ms_p50": round(pre_p50, 4),
+                        "kernel_ms_p95": round(pre_p95, 4), "flops_metric": flops,
+                        "flops_exact": prefill_flops_exact(pc),
+                        "tflops_exact": round(prefill_flops_exact(pc) / (pre_ms * 1e-3) / 1e12, 2),
+                        "algorithmic_bytes": prefill_bytes(pc)},
+            "decode": {"workload": DECODE, "value": round(decode_gbs, 1), "unit": "GB/s",
+                       "split_ms_mean": round(spl_ms, 4), "combine_ms_mean": round(cmb_ms, 4),
+                       "split_ms_p95": round(spl_p95, 4),
+                       "algorithmic_bytes": dbytes,
+                       "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1),
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                                    "traffic": load_traffic("step", "attn_decode_split_kernel", digest)}},
+        })
+        print(f"step: prefill {pre_ms:.4f} ms ({tflops:.1f} TFLOP/s), decode split {spl_ms:.4f} ms "
+              f"({split_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+        del part_o, part_l
+        if cpu:
+            rec["decode"]["cpu_baseline"] = cpu_baseline_decode(dc, budget_s=6.0)
+        del dc, dc_dev
+
+    extra = {}
+    if "c1" in legs:
+        c = W.config_case(NONCAUSAL, device=dev)
+        extra["noncausal_d64"] = fwd_leg(ea, c, NONCAUSAL, "c1", stream, torch, digest, prefill_flops(c),
+                                         prefill_flops_exact(c), prefill_bytes(c), reps=50)
+        extra["noncausal_d64"]["note"] = "16 workgroups of 128 rows on 256 compute units: launch-latency bound"
+        if cpu:
+            extra["noncausal_d64"]["cpu_baseline"] = cpu_baseline_dense(c, NONCAUSAL, budget_s=2.0)
+        del c
+    if "c3" in legs:
+        c = W.config_case(GQA, device=dev)
+        extra["gqa_n8192"] = fwd_leg(ea, c, GQA, "c3", stream, torch, digest, prefill_flops(c),
+                                     prefill_flops_exact(c), prefill_bytes(c))
+        if cpu:
+            extra["gqa_n8192"]["cpu_baseline"] = cpu_baseline_dense(c, GQA, budget_s=8.0)
+        del c
+    for d in (128, 64, 256):
+        leg = f"c4_d{d}"
+        if leg not in legs:
+            continue
+        c = W.config_case(VARLEN, device=dev, d=d)
+        for x in ("cu_seqlens_q", "cu_seqlens_k"):
+            c[x] = c[x].to(dev)
+        extra[f"varlen_d{d}"] = fwd_leg(ea, c, f"{VARLEN} d={d}", leg, stream, torch, digest, varlen_flops(c),
+                                        varlen_flops_exact(c), varlen_bytes(c))
+        extra[f"varlen_d{d}"]["note"] = ("value uses the metric formula (halved for causal); tflops_exact "
+                                         "counts the allowed pairs (bottom-right causal with Nq = Nk/4)")
+        if cpu:
+            extra[f"varlen_d{d}"]["cpu_baseline"] = cpu_baseline_varlen(c, VARLEN, budget_s=5.0)
+        del c
+    for key, leg in extra.items():
+        print(f"{key}: {leg['kernel_ms_mean']:.4f} ms, {leg['value']:.1f} TFLOP/s "
+              f"(exact {leg['tflops_exact']:.1f})", file=sys.stderr, flush=True)
+    rec["configs"] = extra
+
+    bwd = time_backward(ea, pc, out, lse, stream, torch, digest) if "backward" in legs else None
+    kvc = time_decode_kvcache(ea, W, dev, props, stream, torch, digest) if "kvcache" in legs else None
+    fp8 = time_fp8(ea, W, pc, stream, torch, digest) if "fp8" in legs else None
+    ceil = measure_ceilings(ea, torch, dev, stream) if "ceilings" in legs else None
+    rec["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "cus": props.multi_processor_count, "torch": torch.__version__,
+                     "hip": getattr(torch.version, "hip", None)}
+    rec["kernel_source_digest"] = digest
     if ceil is not None:
         rec["ceilings"] = ceil
-        add_measured(rec["roofline"], ceil["mfma_bf16_random_tflops"])
-        add_measured(rec["decode"]["roofline"], ceil["hbm_read_gbs"])
+        for r in [rec.get("roofline")] + [x["roofline"] for x in extra.values()]:
+            add_measured(r, ceil["mfma_bf16_random_tflops"])
+        if "decode" in rec:
+            add_measured(rec["decode"]["roofline"], ceil["hbm_read_gbs"])
         if bwd is not None:
             add_measured(bwd["roofline"], ceil["mfma_bf16_random_tflops"])
         if kvc is not None:
@@ -591,8 +800,8 @@ def main():
         rec["decode_kvcache"] = kvc
     if fp8 is not None:
         rec["fp8_forward"] = fp8
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(pc)
+    if cpu and "step" in legs:
+        rec["cpu_baseline"] = cpu_baseline_dense(pc, PREFILL, budget_s=12.0)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -115,11 +115,15 @@ void attn_decode_split_kernel(DecodeParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run[QB], l_part[QB];
+    // l_part: partial sums of P in fp32 (for lse); lr_part: of P as rounded to
+    // bf16 for the P V product (the partial output's divisor, so the weights
+    // it applies sum to one exactly).
+    float m_run[QB], l_part[QB], lr_part[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m_run[qb] = -INFINITY;
         l_part[qb] = 0.0f;
+        lr_part[qb] = 0.0f;
     }
     const float c2 = p.scale * kLog2e;
 
@@ -213,6 +217,7 @@ void attn_decode_split_kernel(DecodeParams p) {
             if (__builtin_amdgcn_ballot_w64(scale_old)) {
                 const float alpha = scale_old ? exp2f(m_run[qb] - m_new) : 1.0f;
                 l_part[qb] *= alpha;
+                lr_part[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
             }
@@ -230,6 +235,7 @@ void attn_decode_split_kernel(DecodeParams p) {
             l_part[qb] += rs;
             pb[qb] = u32x4{pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]),
                            pack_bf16x2(e[1][0], e[1][1]), pack_bf16x2(e[1][2], e[1][3])};
+            lr_part[qb] = add_bf16x8(pb[qb], lr_part[qb]);
         }
         // ---- O^T += V^T P^T ------------------------------------------------
 #pragma unroll
@@ -257,8 +263,9 @@ void attn_decode_split_kernel(DecodeParams p) {
     for (int qb = 0; qb < QB; ++qb) {
         const int j = 16 * qb + l16;
         const float L = quad_sum(l_part[qb]);
+        const float Lr = quad_sum(lr_part[qb]);
         if (j < g) {
-            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            const float inv = L > 0.0f ? 1.0f / Lr : 0.0f;
             float* orow = p.out_part + (part_row + j) * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {

@@ -18,6 +18,10 @@
 //   than kRescaleThreshold (the conditional rescaling named in "Deep Dive -
 //   FlashAttention", "FA1 through FA4 retune the same IO idea");
 //   P = exp2(S * scale * log2(e) - m), l += rowsum P, O^T += V^T P^T.
+// P enters the matrix product rounded to bf16; the output is divided by the
+// sum of those rounded values (so the weights it applies sum to one exactly:
+// a row dominated by a few keys then loses no accuracy to their rounding),
+// while lse comes from the fp32 sum of the unrounded values.
 // Tiles wholly above the causal boundary are never visited ("FlashAttention:
 // Part 1", section 3.5).  K/V tiles are double-buffered in LDS: the global
 // loads of tile t+1 are issued before tile t is computed.
@@ -241,11 +245,14 @@ void attn_fwd_kernel(FwdParams p) {
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.0f;
-    float m_run[QB], l_part[QB];
+    // l_part: partial row sums of P in fp32 (for lse); lr_part: of P as
+    // rounded to bf16 for the P V product (the output's divisor).
+    float m_run[QB], l_part[QB], lr_part[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m_run[qb] = -INFINITY;
         l_part[qb] = 0.0f;
+        lr_part[qb] = 0.0f;
     }
     const float c2 = p.scale * kLog2e;
 
@@ -326,6 +333,7 @@ void attn_fwd_kernel(FwdParams p) {
                 if (__builtin_amdgcn_ballot_w64(scale_old)) {
                     const float alpha = scale_old ? exp2f(m_run[qb] - m_new) : 1.0f;
                     l_part[qb] *= alpha;
+                    lr_part[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -333,7 +341,7 @@ void attn_fwd_kernel(FwdParams p) {
                 }
                 if (raise) m_run[qb] = m_new;
                 const float shift = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-                float rs = 0.0f;
+                float rs = 0.0f, rr = lr_part[qb];
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -349,9 +357,11 @@ void attn_fwd_kernel(FwdParams p) {
                         for (int j = 0; j < 4; ++j)
                             w[j] = pack_bf16x2(sacc[kb][qb][8 * c + 2 * j], sacc[kb][qb][8 * c + 2 * j + 1]);
                         pb[kb][qb][c] = w;
+                        rr = add_bf16x8(w, rr);
                     }
                 }
                 l_part[qb] += rs;
+                lr_part[qb] = rr;
             }
             // ---- O^T += V^T P^T ----------------------------------------------
 #pragma unroll
@@ -382,8 +392,9 @@ void attn_fwd_kernel(FwdParams p) {
     for (int qb = 0; qb < QB; ++qb) {
         const int row = wr0 + 32 * qb + l32;
         const float l_tot = pair_sum(l_part[qb]);
+        const float lr_tot = pair_sum(lr_part[qb]);
         if (row < Nq) {
-            const float inv = bad ? NAN : (l_tot > 0.0f ? 1.0f / l_tot : 0.0f);
+            const float inv = bad ? NAN : (l_tot > 0.0f ? 1.0f / lr_tot : 0.0f);
             uint16_t* orow = p.out + ((long)(q_off + row) * p.hq + hq) * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)

@@ -64,6 +64,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// acc + the sum of the eight bf16 values packed in w (four pairs), each pair
+// added by one v_dot2c_f32_bf16 against (1, 1): the products are exact and the
+// sum is taken in fp32.  The components are named one by one: indexing w with
+// the counter of an unrolled loop under __builtin_bit_cast made this compiler
+// read w.x four times.
+__device__ __forceinline__ float add_bf16x8(const u32x4& w, float acc) {
+    const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w;
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), one, acc, false);
+    return acc;
+}
+
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

@@ -4,7 +4,7 @@ Tolerances (bf16 out, fp32 lse): max |out - ref| <= 1.5e-2, mean |out - ref|
 <= 1e-3, |lse - ref| <= 1e-3; rows with no allowed key must give out == 0 and
 lse == -inf on both sides.  Small and ragged shapes are compared in full;
 the full-size workloads are launched exactly as the benchmark launches them
-and compared on sampled rows that the oracle computes one by one.
+and compared on every element as well (the oracle computes them in full).
 """
 import math
 
@@ -90,34 +90,19 @@ def test_config_noncausal_mha_full():
     dense_parity(c["B"], c["Nq"], c["Nk"], c["Hq"], c["Hkv"], c["d"], c["causal"], c["seed"])
 
 
-def sample_dense_rows(B, Hq, Nq, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = {(0, 0, 0), (B - 1, Hq - 1, Nq - 1), (0, Hq - 1, Nq // 2), (B - 1, 0, 127),
-            (0, 1 % Hq, 128), (B - 1, Hq // 2, 255), (0, 0, 256)}
-    while len(rows) < n:
-        rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(Nq))))
-    return sorted(r for r in rows if r[2] < Nq)
-
-
 @pytest.mark.parametrize("name", ["mha_causal_b4_h16_n4096_d128", "gqa_causal_b2_hq32_hkv8_n8192_d128_koutliers"])
-def test_config_dense_full_sampled(name):
+def test_config_dense_full(name):
+    """The full-size dense workload, launched as the benchmark launches it, against
+    the oracle on every element (max and mean |diff| over the whole output)."""
     case = W.config_case(name, device=DEV)
     out, lse = ea.attn_fwd(case["q"], case["k"], case["v"], causal=case["causal"],
                            softmax_scale=case["scale"])
     torch.cuda.synchronize()
-    rows = sample_dense_rows(case["B"], case["Hq"], case["Nq"], 96, seed=7)
-    q, k, v = (case[x].to("cpu") for x in "qkv")
-    ref_o, ref_l = oracle.attention_rows(to64(q), to64(k), to64(v), rows, causal=case["causal"],
-                                         softmax_scale=case["scale"])
-    o_cpu = out.to("cpu")
-    got = np.stack([to64(o_cpu[b, i, h]) for b, h, i in rows])
-    lse_cpu = lse.to("cpu")
-    got_l = np.array([float(lse_cpu[b, h, i]) for b, h, i in rows])
-    assert_close(got, got_l, ref_o, ref_l, name)
-    # Properties that hold at any size: finite everywhere, lse finite (every
-    # row of a square causal problem sees at least its own key).
-    assert torch.isfinite(out).all().item()
-    assert torch.isfinite(lse).all().item()
+    ref_o, ref_l = oracle.attention_ref(to64(case["q"]), to64(case["k"]), to64(case["v"]),
+                                        causal=case["causal"], softmax_scale=case["scale"])
+    assert_close(to64(out), to64(lse), ref_o, ref_l, name)
+    # Every row of a square causal problem sees at least its own key.
+    assert np.isfinite(ref_l).all()
 
 
 def varlen_parity(nq, nk, Hq, Hkv, d, causal, seed, sample=None):
@@ -175,10 +160,11 @@ def test_varlen_small_edge_lengths(d):
 
 
 @pytest.mark.parametrize("d", [128, 64, 256])
-def test_config_varlen_chunked_prefill_sampled(d):
+def test_config_varlen_chunked_prefill_full(d):
+    """All 16 packed sequences and all 32 query heads at each head dim, every element."""
     c = W.CONFIGS["varlen_chunked_prefill_16seq_hq32_hkv8"]
     nq, nk = W.varlen_lengths(c["n_seqs"], c["nk_lo"], c["nk_hi"], c["q_div"], c["seed"])
-    varlen_parity(nq, nk, c["Hq"], c["Hkv"], d, True, seed=c["seed"] * 1000 + d, sample=64)
+    varlen_parity(nq, nk, c["Hq"], c["Hkv"], d, True, seed=c["seed"] * 1000 + d)
 
 
 def oracle_decode(case, req):
@@ -247,23 +233,48 @@ def test_decode_odd_head_counts_and_groups(hq, hkv, d):
     decode_parity(W.decode_case(lens, hq, hkv, d, seed=80 + hq + d, poison=True), 1024)
 
 
-def test_config_decode_full_sampled():
+def test_config_decode_full():
+    """All 64 requests of the paged decode workload with the heuristic chunk (the
+    benchmark's launch), against the unsplit oracle; the oracle runs on groups
+    of eight requests to bound host memory."""
     case = W.config_case("paged_decode_b64_hq32_hkv8_d128", device=DEV)
     lens = case["seqlens_k"].tolist()
-    order = np.argsort(lens)
-    req = sorted({int(order[0]), int(order[-1]), 5, 17, 40})
     chunk = ea.attn_decode_default_chunk(case["B"], case["Hkv"], max(lens),
                                          torch.cuda.get_device_properties(0).multi_processor_count)
-    out, lse = decode_parity(case, chunk, requests=req)
-    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+    dev = {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in case.items()}
+    n = max(1, ea.attn_decode_num_splits(max(lens), chunk))
+    po, pl = ea.attn_decode_splitkv(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_table"],
+                                    dev["seqlens_k"], chunk_tokens=chunk, num_splits=n,
+                                    softmax_scale=case["d"] ** -0.5)
+    out, lse = ea.attn_decode_combine(po, pl, dev["seqlens_k"], chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    o_cpu, l_cpu = to64(out), to64(lse)
+    ref_o = np.zeros_like(o_cpu)
+    ref_l = np.zeros_like(l_cpu)
+    for g0 in range(0, case["B"], 8):
+        req = list(range(g0, min(case["B"], g0 + 8)))
+        ref_o[req], ref_l[req] = oracle_decode(case, req)
+    assert_close(o_cpu, l_cpu, ref_o, ref_l, f"decode workload chunk {chunk}")
 
 
 def test_decode_chunk_invariance():
-    """Different split counts agree with each other (and with the oracle above)."""
+    """Different split counts agree with each other (and with the oracle above).
+
+    Chunkings differ in where each chunk's softmax shift sits, so the bf16
+    rounding of the probabilities falls differently; each chunk divides by
+    the sum of its rounded probabilities and the combine is fp32.  They must
+    agree within the oracle bar itself (not twice it), with mean |diff|
+    <= 1e-4 and lse within 1e-4."""
     case = W.decode_case([5000, 17, 2300, 4096], 8, 2, 128, seed=71)
-    outs = [decode_parity(case, c)[0].float() for c in (256, 768, 4096, 8192)]
-    for o in outs[1:]:
-        assert (o - outs[0]).abs().max().item() <= 2 * OUT_MAX_ABS
+    runs = [decode_parity(case, c) for c in (256, 768, 4096, 8192)]
+    o0, l0 = runs[0][0].float(), runs[0][1]
+    for o, l in runs[1:]:
+        d = (o.float() - o0).abs()
+        print(f"chunk invariance: max {d.max().item():.3e} mean {d.mean().item():.3e} "
+              f"lse {(l - l0).abs().max().item():.3e}")
+        assert d.max().item() <= OUT_MAX_ABS
+        assert d.mean().item() <= 1e-4
+        assert (l - l0).abs().max().item() <= 1e-4
 
 
 def test_mixed_shape_order_is_stable():
