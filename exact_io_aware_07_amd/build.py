@@ -15,6 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+# Check build for the tests: the forward kernel with one LDS stage (tiles are
+# loaded only after every wave has finished the previous one); its results must
+# equal libattn.so's bit for bit.
+LIB_SINGLE_STAGE = os.path.join(PKG, "libattn_single_stage.so")
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fp8.hip", "attn_ceiling.hip", "attn_api.hip"]
 ARCH = "gfx950"
 
@@ -33,8 +37,8 @@ def hipcc():
     return path
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src, extra, obj_name=None):
+    obj = os.path.join(BUILD, obj_name or os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + HIPFLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -44,24 +48,38 @@ def _compile(src, extra):
     return obj, msgs
 
 
-def build(verbose=False, extra_flags=(), out=LIB):
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra_flags)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    objs = [o for o, _ in results]
-    if verbose:
-        for _, m in results:
-            if m.strip():
-                print(m)
+def _link(objs, out):
     tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, out)
+
+
+def build(verbose=False, extra_flags=(), out=LIB, single_stage=True):
+    """Compile every source into `out`; with single_stage, also link the
+    single-stage check library (the forward kernel rebuilt with one LDS stage)."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra_flags)
+    jobs = [(s, extra, None) for s in SOURCES]
+    if single_stage:
+        jobs.append(("attn_fwd.hip", extra + ["-DATTN_FWD_SINGLE_STAGE=1"], "attn_fwd_single_stage.o"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        results = list(ex.map(lambda j: _compile(*j), jobs))
+    objs = [o for o, _ in results[:len(SOURCES)]]
+    if verbose:
+        for _, m in results:
+            if m.strip():
+                print(m)
+    _link(objs, out)
     if verbose:
         print(f"built {out}")
+    if single_stage:
+        ss = [results[-1][0] if os.path.basename(o) == "attn_fwd.o" else o for o in objs]
+        _link(ss, LIB_SINGLE_STAGE)
+        if verbose:
+            print(f"built {LIB_SINGLE_STAGE}")
     return out
 
 

@@ -34,6 +34,15 @@ namespace attn {
 // Page size of the paged prefill's cache (as the paged decode).
 constexpr int kFwdPage = 256;
 
+// ATTN_FWD_SINGLE_STAGE=1 builds a check variant with one LDS stage: each
+// tile's loads are issued only after every wave has finished the previous
+// tile, so no load can overlap a read of the same stage.  Its results must
+// equal the double-buffered kernel's bit for bit (same arithmetic in the same
+// order); a difference would expose a race on the LDS stages.
+#ifndef ATTN_FWD_SINGLE_STAGE
+#define ATTN_FWD_SINGLE_STAGE 0
+#endif
+
 // K fragment reads issued ahead of the first score MFMA of a tile.
 #ifndef ATTN_FWD_K_LEAD
 #define ATTN_FWD_K_LEAD 8
@@ -267,7 +276,7 @@ void attn_fwd_kernel(FwdParams p) {
     auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
         const char* ks = cur;
         const char* vs = cur + Tile::K_BYTES;
-        if (t + 1 < t_end) {
+        if (!ATTN_FWD_SINGLE_STAGE && t + 1 < t_end) {
             issue_tile(t + 1, phys_next, lds_addr(nxt));
             if (PAGED && t + 2 < t_end) phys_next = page_of(t + 2);
         }
@@ -375,14 +384,24 @@ void attn_fwd_kernel(FwdParams p) {
                         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(a, pb[kb][qb][c], oacc[db][qb]);
                     }
         }
+        if (ATTN_FWD_SINGLE_STAGE && t + 1 < t_end) {
+            // Check variant: every wave is done with the stage before it is refilled.
+            __syncthreads();
+            issue_tile(t + 1, phys_next, lds_addr(cur));
+            if (PAGED && t + 2 < t_end) phys_next = page_of(t + 2);
+        }
         // The next tile's loads (this wave's share) must have landed in LDS
         // before the barrier releases other waves to read them.
         wait_vmem();
         __syncthreads();
     };
-    for (int t = t_lo; t < t_end; t += 2) {
-        step(t, stage0, stage1);
-        if (t + 1 < t_end) step(t + 1, stage1, stage0);
+    if constexpr (ATTN_FWD_SINGLE_STAGE) {
+        for (int t = t_lo; t < t_end; ++t) step(t, stage0, stage0);
+    } else {
+        for (int t = t_lo; t < t_end; t += 2) {
+            step(t, stage0, stage1);
+            if (t + 1 < t_end) step(t + 1, stage1, stage0);
+        }
     }
 
     // ---- epilogue: out = O / l (bf16, round to nearest even), lse in nats ----

@@ -13,20 +13,20 @@ ROW_BLOCK = 2048
 
 
 def kv_head_for_queries(num_heads_q, num_heads_kv):
-    """Map each query head to its key/value head.
+    """K/V head of each query head, as a list.
 
     "Deep Dive - FlashAttention", "The public interface is several kernels":
-    consecutive groups of query heads share one K/V head (six Q heads over two
-    K/V heads map as 0,0,0,1,1,1), and the head counts must be positive with
-    the K/V count dividing the Q count ("FlashAttention: Part 1", section 4.1).
+    query heads are shared out in consecutive equal groups (six query heads
+    over two K/V heads give 0,0,0,1,1,1), so query head h reads K/V head
+    floor(h * Hkv / Hq); "FlashAttention: Part 1", section 4.1: Hkv must
+    divide Hq.  Non-integer or non-positive counts are refused.
     """
-    for h in (num_heads_q, num_heads_kv):
-        if type(h) is not int or h <= 0:
-            raise ValueError("head counts must be positive integers")
-    if num_heads_q % num_heads_kv:
-        raise ValueError("K/V head count must divide the query head count")
-    group = num_heads_q // num_heads_kv
-    return [hq // group for hq in range(num_heads_q)]
+    counts = (num_heads_q, num_heads_kv)
+    if not all(isinstance(c, (int, np.integer)) and not isinstance(c, bool) and c >= 1 for c in counts):
+        raise ValueError(f"need integer head counts >= 1, got {counts}")
+    if num_heads_q % num_heads_kv != 0:
+        raise ValueError(f"{num_heads_kv} K/V heads do not split {num_heads_q} query heads into equal groups")
+    return [int(x) for x in (np.arange(num_heads_q) * num_heads_kv) // num_heads_q]
 
 
 def causal_keep(seqlen_q, seqlen_k):

@@ -982,13 +982,96 @@ def check_fp8_attention_and_bound():
             assert np.max(bound[:, rows]) < 0.2
 
 
+def check_fp8_bound_informative():
+    """fp8_out_bound must be tight enough to mean something, not only an upper
+    bound: on random data (the four causal / turn combinations of
+    check_fp8_attention_and_bound) the slow tile model of the kernel's
+    probability rounding reaches at least 0.2 of the bound somewhere and its
+    mean error at least 0.03 of the mean bound; and on a constructed row whose
+    scaled probabilities (64 * p = 1.4 * 2^-10) all fall at the same point of
+    the E4M3 subnormal grid, so that their rounding errors add up, the model
+    error reaches at least 0.35 of the bound.  A bound four times too loose,
+    or a sub-2^-6 term built from a probability scale four times too small,
+    fails these floors (measured: 0.26-0.55, 0.062-0.076 and 0.55)."""
+    from fp8_tile_model import fp8_tiled_attention
+    rng = np.random.default_rng(59)
+    B, N, Hq, Hkv, d = 1, 150, 2, 1, 128
+    q = rng.standard_normal((B, N, Hq, d))
+    k = rng.standard_normal((B, N, Hkv, d))
+    v = rng.standard_normal((B, N, Hkv, d))
+    v[0, 64:128] *= 0.01
+    v[0, 128:] = 0.0
+    s = rng.choice([-1.0, 1.0], size=d)
+    rows = [0, 1, 63, 64, 100, 149]
+    for causal in (True, False):
+        for inc in (False, True):
+            sg = s if inc else None
+            qc, qs = OF.quantize_blocks(q, sg)
+            kc, ks = OF.quantize_blocks(k, sg)
+            vc, vs = OF.quantize_blocks(v, None)
+            kw = dict(causal=causal, softmax_scale=d ** -0.5, incoherent=inc)
+            ref, _ = OF.attention_fp8_ref(qc, kc, vc, qs, ks, vs, **kw)
+            bound = OF.fp8_out_bound(qc, kc, vc, qs, ks, vs, **kw)[:, rows]
+            err = np.abs(fp8_tiled_attention(qc, kc, vc, qs, ks, vs, rows=rows, **kw)[:, rows] - ref[:, rows])
+            assert np.max(err / np.maximum(bound, 1e-300)) >= 0.2, (causal, inc)
+            assert err.mean() >= 0.03 * bound.mean(), (causal, inc)
+    n = 60
+    q = np.zeros((1, 1, 1, d))
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, n + 1, 1, d))
+    k[0, 1:, 0, 0] = np.log(1.4 * 2.0 ** -16) * d ** 0.5  # score log(p) with 64 p = 1.4 * 2^-10
+    v = np.ones((1, n + 1, 1, d))
+    v[0, 0] = 0.0
+    qc, qs = OF.quantize_blocks(q, None)
+    kc, ks = OF.quantize_blocks(k, None)
+    vc, vs = OF.quantize_blocks(v, None)
+    kw = dict(causal=False, softmax_scale=d ** -0.5, incoherent=False)
+    ref, _ = OF.attention_fp8_ref(qc, kc, vc, qs, ks, vs, **kw)
+    bound = OF.fp8_out_bound(qc, kc, vc, qs, ks, vs, **kw)
+    err = np.abs(fp8_tiled_attention(qc, kc, vc, qs, ks, vs, **kw) - ref)
+    assert np.all(err <= bound * (1 + 1e-9))
+    assert np.max(err / bound) >= 0.35
+
+
+def check_fp8_incoherence_helps_feature_outliers():
+    """Incoherent processing lowers the error of attention on the quantised
+    operands ("FlashAttention-3 and PagedAttention: IO-Aware Attention Kernels
+    (2026)", "FlashAttention-3": the random orthogonal transform spreads
+    outliers before quantisation; the page quotes a 2.6x lower error).  With
+    four feature channels of Q and K twenty times larger than the rest, the
+    mean error against the unquantised fp64 definition must drop by at least
+    a third with the turn (measured 2.7x); a block with one key row three
+    times larger is not helped (the turn mixes the features of a row, not the
+    rows of a block), which is why the key-outlier workload is not used here."""
+    rng = np.random.default_rng(61)
+    B, Nq, Nk, Hq, Hkv, d = 1, 128, 256, 2, 2, 128
+    q = rng.standard_normal((B, Nq, Hq, d))
+    k = rng.standard_normal((B, Nk, Hkv, d))
+    v = rng.standard_normal((B, Nk, Hkv, d))
+    ch = rng.choice(d, size=4, replace=False)
+    q[..., ch] *= 20.0
+    k[..., ch] *= 20.0
+    o, _ = OA.attention_ref(q, k, v, causal=True, softmax_scale=d ** -0.5)
+    s = rng.choice([-1.0, 1.0], size=d)
+    errs = []
+    for sg in (None, s):
+        qc, qs = OF.quantize_blocks(q, sg)
+        kc, ks = OF.quantize_blocks(k, sg)
+        vc, vs = OF.quantize_blocks(v, None)
+        o8, _ = OF.attention_fp8_ref(qc, kc, vc, qs, ks, vs, causal=True, softmax_scale=d ** -0.5,
+                                     incoherent=sg is not None)
+        errs.append(np.mean(np.abs(o8 - o)))
+    assert errs[1] <= (2.0 / 3.0) * errs[0], errs
+
+
 ALL_CHECKS = [
     check_two_tiles_printed, check_tile_states, check_tiles_and_shifts, check_masked_rows,
     check_causal_masks_printed, check_gqa_printed, check_rows_sum_to_one, check_closed_forms,
     check_brute_force, check_sdpa_fp64, check_paged, check_split_combine,
     check_numpy_tiled_exactness, check_varlen_packing, check_rows_api,
     check_bwd_sdpa_fp64, check_bwd_finite_differences, check_bwd_identities,
-    check_bwd_gqa_and_packing, check_window_forms, check_window_brute_force, check_paged_prefill,
+    check_bwd_gqa_and_packing, check_window_forms, check_fp8_bound_informative,
+    check_fp8_incoherence_helps_feature_outliers, check_window_brute_force, check_paged_prefill,
     check_round_bf16, check_rotary_quarter_turns, check_rotary_relative_position, check_rotary_f32,
     check_append, check_decode_append,
     check_e4m3_codec, check_fwht, check_quantize_blocks, check_vt_layout, check_fp8_attention_and_bound,

@@ -292,6 +292,7 @@ _orig_quant = OF.quantize_blocks
 _orig_vtkey = OF.vt_key_of_position
 _orig_dequant = OF.dequantize
 _orig_fp8_attn = OF.attention_fp8_ref
+_orig_fp8_bound = OF.fp8_out_bound
 
 
 def _encode_rounding(fn):
@@ -359,6 +360,9 @@ FP8_MUTANTS = {
     "dequantize_block_off_by_one_row": ("dequantize", _dequant_off_by_one_row),
     "fp8_attention_scale_not_divided": ("attention_fp8_ref",
                                         lambda *a, **kw: _orig_fp8_attn(*a, **dict(kw, incoherent=False))),
+    # A bound that is too loose must be caught as well as one that is too tight.
+    "fp8_bound_four_times_looser": ("fp8_out_bound", lambda *a, **kw: 4.0 * _orig_fp8_bound(*a, **kw)),
+    "fp8_bound_probability_scale_16": ("P_SCALE", 16.0),
 }
 
 

@@ -1,12 +1,13 @@
-"""A test-only float64 tiled forward, written from the online-softmax recurrence.
+"""A test-only float64 tiled forward, built on the state merge of online softmax.
 
-"Flash Attention: A Complete Architectural Autopsy", "The Online Softmax
-Recurrence": per key block t, m_t = max(m_{t-1}, rowmax S_t),
-P_t = exp(S_t - m_t), l_t = exp(m_{t-1} - m_t) l_{t-1} + rowsum P_t,
-O_t = exp(m_{t-1} - m_t) O_{t-1} + P_t V_t, and finally O = O / l.
-"Deep Dive - FlashAttention", "Online softmax is what makes the tiles exact":
-start from m = -inf, l = 0, u = 0 and skip a block with no allowed key before
-any exponential; an entirely masked row returns zeros.
+Each key block on its own has a state (m, l, u): its largest score m, the sum
+l of exp(s - m) and the sum u of exp(s - m) v.  Two states combine exactly
+into the state of their union by bringing both to the larger maximum
+("Flash Attention: A Complete Architectural Autopsy", "The Online Softmax
+Recurrence": the factor exp(m_old - m_new) applied to the running sums;
+"Deep Dive - FlashAttention", "Online softmax is what makes the tiles
+exact").  A block with no allowed key has the empty state, which changes
+nothing; a row whose blocks are all empty returns zeros.
 
 This is separate code from the oracle (it never calls it); tests compare the
 two to pin the oracle's two-pass softmax to the streaming identity.
@@ -15,25 +16,48 @@ import math
 
 import numpy as np
 
+EMPTY = (-math.inf, 0.0, None)
+
+
+def block_state(scores, values):
+    """(m, l, u) of one key block; EMPTY when no score is finite."""
+    ok = np.isfinite(scores)
+    if not ok.any():
+        return EMPTY
+    top = float(scores[ok].max())
+    weights = np.zeros(len(scores))
+    weights[ok] = np.exp(scores[ok] - top)
+    return top, float(weights.sum()), weights @ values
+
+
+def merge_states(run, blk):
+    """The state of two blocks taken together, and the factor the running
+    state was multiplied by (0 when it was empty)."""
+    m_run, l_run, u_run = run
+    m_blk, l_blk, u_blk = blk
+    if m_blk == -math.inf:
+        return run, 1.0
+    if m_run == -math.inf:
+        return (m_blk, l_blk, u_blk.copy()), 0.0
+    top = max(m_run, m_blk)
+    f_run, f_blk = math.exp(m_run - top), math.exp(m_blk - top)
+    return (top, f_run * l_run + f_blk * l_blk, f_run * u_run + f_blk * u_blk), f_run
+
 
 def tiled_row(scores, values, tile, trace=None):
-    """One query row: scores [n] (finite or -inf), values [n, dv]."""
+    """One query row: scores [n] (finite or -inf), values [n, dv].  Returns
+    (out, lse); `trace` collects the running state after each non-empty block."""
     scores = np.asarray(scores, dtype=np.float64)
     values = np.asarray(values, dtype=np.float64)
-    m, l = -math.inf, 0.0
-    u = np.zeros(values.shape[1])
+    state = EMPTY
     for start in range(0, len(scores), tile):
-        s = scores[start:start + tile]
-        if not np.any(np.isfinite(s)):
+        blk = block_state(scores[start:start + tile], values[start:start + tile])
+        if blk is EMPTY:
             continue
-        m_new = max(m, float(s.max()))
-        alpha = 0.0 if m == -math.inf else math.exp(m - m_new)
-        w = np.exp(s - m_new)
-        l = alpha * l + float(w.sum())
-        u = alpha * u + w @ values[start:start + tile]
+        state, factor = merge_states(state, blk)
         if trace is not None:
-            trace.append(dict(m=m_new, l=l, u=u.copy(), alpha=alpha))
-        m = m_new
+            trace.append(dict(m=state[0], l=state[1], u=state[2].copy(), alpha=factor))
+    m, l, u = state
     if l == 0.0:
         return np.zeros(values.shape[1]), -math.inf
     return u / l, m + math.log(l)
