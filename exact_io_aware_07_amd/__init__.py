@@ -28,7 +28,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libattn.so")
+# EXACT_ATTN_LIBRARY selects another build of the same sources (the tests run
+# the ABI checks against a host-sanitizer build this way).
+lib_path = os.environ.get("EXACT_ATTN_LIBRARY") or os.path.join(_HERE, "libattn.so")
 
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",

@@ -83,6 +83,44 @@ def build(verbose=False, extra_flags=(), out=LIB, single_stage=True):
     return out
 
 
+def asan_runtime():
+    """The clang AddressSanitizer runtime shipped with the HIP toolchain."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found under /opt/rocm/lib/llvm")
+    return hits[-1]
+
+
+def build_asan(verbose=False):
+    """Host code instrumented with AddressSanitizer (device code unchanged), into
+    _build/asan/libattn_asan.so, for running the host-side ABI checks; load it
+    with the runtime preloaded (LD_PRELOAD=asan_runtime())."""
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    flags = "-O1 -g -Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+    base = [f for f in HIPFLAGS if f != "-O3"]
+
+    def comp(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        r = subprocess.run([hipcc()] + base + flags + ["-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (asan) failed for {src}:\n{r.stderr[-4000:]}")
+        return obj
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    out = os.path.join(out_dir, "libattn_asan.so")
+    link = "-shared -fPIC -Xarch_host -fsanitize=address".split()
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}"] + link + objs + ["-o", out], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (asan) failed:\n{r.stderr[-4000:]}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
