@@ -48,6 +48,10 @@ constexpr int kFwdPage = 256;
 #define ATTN_FWD_K_LEAD 8
 #endif
 
+// Packed batches of at most this many sequences run their work items longest
+// sequence first (see the work-item mapping in attn_fwd_kernel).
+constexpr int kLengthOrderMax = 64;
+
 // LDS that holds the Q^T fragments a wave parks outside its registers (one
 // object per instantiation that uses it).
 template <int BYTES>
@@ -97,10 +101,10 @@ void attn_fwd_kernel(FwdParams p) {
     int qt, b, hq;
     if constexpr (VARLEN) {
         // Sequences differ in length, so a block of whole sequences per XCD
-        // would load the XCDs unevenly.  Work items (query tile, sequence)
-        // run in query-tile-descending order and the query heads of each
-        // item are spread over the XCDs: XCD x takes heads
-        // [x*hq/8, (x+1)*hq/8), which also keeps a GQA group on one L2.
+        // would load the XCDs unevenly: the query heads of each work item
+        // (query tile, sequence) are spread over the XCDs instead (XCD x
+        // takes heads [x*hq/8, (x+1)*hq/8), which also keeps a GQA group on
+        // one L2), and every XCD runs all items.
         int item;
         if ((p.hq & 7) == 0) {
             const int hpx = p.hq >> 3, x = bid & 7, kk = bid >> 3;
@@ -110,8 +114,65 @@ void attn_fwd_kernel(FwdParams p) {
             item = bid / p.hq;
             hq = bid % p.hq;
         }
-        qt = p.n_qtiles - 1 - item / p.batch;
-        b = item % p.batch;
+        if (p.batch <= kLengthOrderMax) {
+            // Items run longest sequence first (more keys, ties by index),
+            // each sequence's query tiles last tile first.  A tile's work is
+            // mostly its sequence's key prefix, so this is close to a
+            // longest-first schedule, and the tiles of one sequence run
+            // together while its K/V is in L2.  Every workgroup ranks the
+            // sequences itself (one thread per sequence, then a wave scan of
+            // the tile counts in rank order).
+            __shared__ int s_len[kLengthOrderMax];
+            __shared__ int s_order[kLengthOrderMax];
+            __shared__ int s_first[kLengthOrderMax + 1];
+            if (tid < p.batch) {
+                const int kl = PAGED ? p.seqlens_k[tid] : p.cu_k[tid + 1] - p.cu_k[tid];
+                s_len[tid] = kl;
+            }
+            __syncthreads();
+            if (tid < p.batch) {
+                const int mine = s_len[tid];
+                int rank = 0;
+                for (int o = 0; o < p.batch; ++o) {
+                    const int other = s_len[o];
+                    rank += (other > mine) || (other == mine && o < tid);
+                }
+                s_order[rank] = tid;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                int tiles = 0;
+                if (lane < p.batch) {
+                    const int s = s_order[lane];
+                    const int nq = p.cu_q[s + 1] - p.cu_q[s];
+                    tiles = nq > 0 ? (nq + BR - 1) / BR : 0;
+                }
+                int incl = tiles;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(incl, off);
+                    if (lane >= off) incl += y;
+                }
+                if (lane < p.batch) s_first[lane + 1] = incl;
+                if (lane == 0) s_first[0] = 0;
+            }
+            __syncthreads();
+            if (item >= s_first[p.batch]) {
+                b = 0;
+                qt = p.n_qtiles;  // past every sequence: no work
+            } else {
+                int lo = 0, hi = p.batch - 1;  // last rank r with s_first[r] <= item
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_first[mid] <= item) lo = mid; else hi = mid - 1;
+                }
+                b = s_order[lo];
+                qt = (s_first[lo + 1] - s_first[lo]) - 1 - (item - s_first[lo]);
+            }
+        } else {
+            qt = p.n_qtiles - 1 - item / p.batch;
+            b = item % p.batch;
+        }
     } else {
         // Equal-length sequences: when the (sequence, head) count is a
         // multiple of 8, all query tiles of a head run on the same XCD, so
