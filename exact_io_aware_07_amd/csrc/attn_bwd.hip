@@ -24,6 +24,8 @@
 // All products are bf16 MFMA with fp32 accumulation; P and dS are rounded to
 // bf16 as the forward rounds P.
 
+#include <type_traits>
+
 #include "attn_tile.h"
 #include "attn_launch.h"
 
@@ -394,6 +396,7 @@ void attn_bwd_dkdv_pair_kernel(BwdParams p) {
     constexpr uint32_t XBYTES = 2 * 16 * 64 * 4;            // P of one pair: 2 blocks x 16 floats x 64 lanes
     __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage2[D == 128 ? STAGE : 16];  // d = 128 only
     __shared__ __attribute__((aligned(1024))) char xchg[NP * XBYTES];
 
     const int tid = threadIdx.x;
@@ -478,88 +481,173 @@ void attn_bwd_dkdv_pair_kernel(BwdParams p) {
     wait_vmem();
     __syncthreads();
 
-    auto step = [&](int it, char* cur, char* nxt) __attribute__((always_inline)) {
-        if (it + 1 < n_it) issue(it + 1, nxt);
-        const int qs = (qb_lo + it % n_qb) * QBLK;
-        const bool active = kw0 < Nk && (!CAUSAL || qs + QBLK - 1 >= kw0 - shift);
-        const char* qt = cur;
-        const char* gt = cur + Tile::A_BYTES;
-        const float* lv = reinterpret_cast<const float*>(cur + Tile::BYTES);
-        f32x16 sacc[2];
-        u32x4 pw[2][2];  // packed P (P side) or dS (dS side) B operands
-        // ---- phase 1: S and P (P side) / dP (dS side) ----------------------
-        if (active) {
+    // Phase 1 products of block it: S^T = K Q^T (P side) or dP^T = V G^T (dS
+    // side), two accumulation chains interleaved, the LDS reads of the Q (G)
+    // rows kept six products ahead.
+    auto phase1_products = [&](const char* rows, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.0f;
 #pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    sacc[rb] = mfma32(rd_row<D>(side_p ? qt : gt, rb, s, lane), kv[s], sacc[rb]);
-            }
-            if (side_p) {
-                const bool need_mask = (qs + QBLK > Nq) || (kw0 + 31 >= Nk) ||
-                                       (CAUSAL && kw0 + 31 > qs + shift);
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    if (need_mask) {
+            for (int rb = 0; rb < 2; ++rb) sacc[rb] = mfma32(rd_row<D>(rows, rb, s, lane), kv[s], sacc[rb]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS read
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int i = qs + 32 * rb + acc_row(r, lane);
-                            const bool keep = i < Nq && key < Nk && (!CAUSAL || key <= i + shift);
-                            if (!keep) sacc[rb][r] = -INFINITY;
-                        }
-                    }
-                    // lse2 of the 16 rows this lane holds: rows 32 rb + 8 q4 + 4 (l / 32) .. + 3.
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4 l2 = *reinterpret_cast<const f32x4*>(lv + 32 * rb + 8 * q4 + 4 * (lane >> 5));
-                        f32x4 pr;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            pr[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * q4 + j], c2, -l2[j]));
-                            sacc[rb][4 * q4 + j] = pr[j];
-                        }
-                        xp[(rb * 4 + q4) * 64 + lane] = pr;
-                    }
-                    pack_acc(sacc[rb], pw[rb]);
-                }
-            }
+        for (int i = 0; i < 2 * KS - 6; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        // P is in LDS for the dS side.
-        __syncthreads();
-        // ---- phase 2: dV (P side) / dS and dK (dS side) --------------------
-        if (active) {
-            if (!side_p) {
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4 pr = xp[(rb * 4 + q4) * 64 + lane];
-                        const f32x4 dd = *reinterpret_cast<const f32x4*>(lv + QBLK + 32 * rb + 8 * q4 + 4 * (lane >> 5));
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            sacc[rb][4 * q4 + j] = pr[j] * (sacc[rb][4 * q4 + j] - dd[j]);
-                    }
-                    pack_acc(sacc[rb], pw[rb]);
-                }
-            }
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        acc[db] = mfma32(rd_tr<D>(side_p ? gt : qt, db, rb, c, lane), pw[rb][c], acc[db]);
-        }
-        // The next tile has landed, and the dS side has read P before the P
-        // side overwrites it.
-        wait_vmem();
-        __syncthreads();
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     };
-    for (int it = 0; it < n_it; it += 2) {
-        step(it, stage0, stage1);
-        if (it + 1 < n_it) step(it + 1, stage1, stage0);
+    // P side, after phase 1: mask, P = exp2(S scale log2e - lse2), P to LDS
+    // for the dS side, and P as bf16 B operands.
+    auto make_p = [&](int qs, const float* lv, f32x16 (&sacc)[2], u32x4 (&pw)[2][2]) __attribute__((always_inline)) {
+        const bool need_mask = (qs + QBLK > Nq) || (kw0 + 31 >= Nk) || (CAUSAL && kw0 + 31 > qs + shift);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = qs + 32 * rb + acc_row(r, lane);
+                    const bool keep = i < Nq && key < Nk && (!CAUSAL || key <= i + shift);
+                    if (!keep) sacc[rb][r] = -INFINITY;
+                }
+            }
+            // lse2 of the 16 rows this lane holds: rows 32 rb + 8 q4 + 4 (l / 32) .. + 3.
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 l2 = *reinterpret_cast<const f32x4*>(lv + 32 * rb + 8 * q4 + 4 * (lane >> 5));
+                f32x4 pr;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pr[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * q4 + j], c2, -l2[j]));
+                    sacc[rb][4 * q4 + j] = pr[j];
+                }
+                xp[(rb * 4 + q4) * 64 + lane] = pr;
+            }
+            pack_acc(sacc[rb], pw[rb]);
+        }
+    };
+    // dS side, after the barrier: dS = P o (dP - D) as bf16 B operands.
+    auto make_ds = [&](const float* lv, f32x16 (&sacc)[2], u32x4 (&pw)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 pr = xp[(rb * 4 + q4) * 64 + lane];
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(lv + QBLK + 32 * rb + 8 * q4 + 4 * (lane >> 5));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sacc[rb][4 * q4 + j] = pr[j] * (sacc[rb][4 * q4 + j] - dd[j]);
+            }
+            pack_acc(sacc[rb], pw[rb]);
+        }
+    };
+    // acc += rows^T B over the block's 64 rows: dV^T += G^T P or dK^T += Q^T dS,
+    // the transposed LDS reads kept two products ahead.
+    auto phase2_products = [&](const char* rows, const u32x4 (&pw)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] = mfma32(rd_tr<D>(rows, db, rb, c, lane), pw[rb][c], acc[db]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 4 * DB - 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    };
+
+    if constexpr (D == 128) {
+        // Three stages.  The dS side adds dK^T for block it-1 in phase 1 of
+        // step it, beside its own dP products and the P side's exponentials,
+        // from that block's dS (kept in registers) and stage (the loads of
+        // block it+1 go to the third stage).  Each side runs its own copy of
+        // the loop, with the same barriers, so that registers one side needs
+        // are not held on the other.  The order of accumulation into dK is
+        // unchanged: bitwise-identical gradients.
+        auto run = [&](auto side) __attribute__((always_inline)) {
+            constexpr bool SP = decltype(side)::value;
+            u32x4 ds_prev[2][2];
+            bool act_prev = false;
+            const char* qt_prev = stage0;
+            auto step = [&](int it, char* cur, char* nxt) __attribute__((always_inline)) {
+                if (it + 1 < n_it) issue(it + 1, nxt);
+                const int qs = (qb_lo + it % n_qb) * QBLK;
+                const bool active = kw0 < Nk && (!CAUSAL || qs + QBLK - 1 >= kw0 - shift);
+                const char* qt = cur;
+                const char* gt = cur + Tile::A_BYTES;
+                const float* lv = reinterpret_cast<const float*>(cur + Tile::BYTES);
+                f32x16 sacc[2];
+                u32x4 pw[2][2];
+                if (active) {
+                    phase1_products(SP ? qt : gt, sacc);
+                    if constexpr (SP) make_p(qs, lv, sacc, pw);
+                }
+                if constexpr (!SP) {
+                    if (act_prev) phase2_products(qt_prev, ds_prev);
+                }
+                // P is in LDS for the dS side.
+                __syncthreads();
+                if (active) {
+                    if constexpr (SP)
+                        phase2_products(gt, pw);
+                    else
+                        make_ds(lv, sacc, ds_prev);
+                }
+                act_prev = active;
+                qt_prev = qt;
+                // The next block has landed, and the dS side has read P
+                // before the P side overwrites it.
+                wait_vmem();
+                __syncthreads();
+            };
+            for (int it = 0; it < n_it; it += 3) {
+                step(it, stage0, stage1);
+                if (it + 1 < n_it) step(it + 1, stage1, stage2);
+                if (it + 2 < n_it) step(it + 2, stage2, stage0);
+            }
+            if constexpr (!SP) {
+                if (act_prev) phase2_products(qt_prev, ds_prev);
+            }
+        };
+        if (side_p)
+            run(std::true_type{});
+        else
+            run(std::false_type{});
+    } else {
+        // d = 256: two stages (three do not fit the LDS); both products of a
+        // side within its step.
+        auto step = [&](int it, char* cur, char* nxt) __attribute__((always_inline)) {
+            if (it + 1 < n_it) issue(it + 1, nxt);
+            const int qs = (qb_lo + it % n_qb) * QBLK;
+            const bool active = kw0 < Nk && (!CAUSAL || qs + QBLK - 1 >= kw0 - shift);
+            const char* qt = cur;
+            const char* gt = cur + Tile::A_BYTES;
+            const float* lv = reinterpret_cast<const float*>(cur + Tile::BYTES);
+            f32x16 sacc[2];
+            u32x4 pw[2][2];  // packed P (P side) or dS (dS side) B operands
+            if (active) {
+                phase1_products(side_p ? qt : gt, sacc);
+                if (side_p) make_p(qs, lv, sacc, pw);
+            }
+            // P is in LDS for the dS side.
+            __syncthreads();
+            if (active) {
+                if (!side_p) make_ds(lv, sacc, pw);
+                phase2_products(side_p ? gt : qt, pw);
+            }
+            wait_vmem();
+            __syncthreads();
+        };
+        for (int it = 0; it < n_it; it += 2) {
+            step(it, stage0, stage1);
+            if (it + 1 < n_it) step(it + 1, stage1, stage0);
+        }
     }
 
     if (key < Nk) {
@@ -687,6 +775,16 @@ void attn_bwd_dq_kernel(BwdParams p) {
                     sacc = mfma32(rd_row<D>(ks, kb, s, lane), qf[s], sacc);
                     pacc = mfma32(rd_row<D>(vs, kb, s, lane), gf[s], pacc);
                 }
+                if constexpr (D != 256) {  // (at d = 256 the reads ahead would spill)
+                    // K and V row reads kept six products ahead.
+                    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+                    for (int i = 0; i < 2 * KS - 6; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+                }
                 if (need_mask) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
@@ -704,6 +802,16 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
                         dacc[db] = mfma32(rd_tr<D>(ks, db, kb, c, lane), pds[c], dacc[db]);
+                if constexpr (D != 256) {
+                    // Transposed K reads kept three products ahead.
+                    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+                    for (int i = 0; i < 2 * DB - 3; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+                }
             }
         }
         wait_vmem();
