@@ -323,6 +323,14 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
                     sacc = mfma32(rd_row<D>(qt, rb, s, lane), kf[s], sacc);
                     pacc = mfma32(rd_row<D>(gt, rb, s, lane), vf[s], pacc);
                 }
+                // Q and G row reads kept six products ahead.
+                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+                for (int i = 0; i < 2 * KS - 6; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
                 // lse2 and D of the 16 rows this lane holds: rows 32 rb + 8 q4 + 4 (l / 32) .. + 3.
                 f32x4 l2[4], dd[4];
 #pragma unroll
@@ -355,6 +363,14 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
                         dv[db] = mfma32(rd_tr<D>(gt, db, rb, c, lane), pp[c], dv[db]);
                         dk[db] = mfma32(rd_tr<D>(qt, db, rb, c, lane), pds[c], dk[db]);
                     }
+                // Transposed reads kept two products ahead.
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 4 * DB - 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
         }
         wait_vmem();
