@@ -19,7 +19,7 @@ packed chunked prefill at d = 128, 64 and 256, and the widened rows (backward,
 decode with append + rotary, FP8 forward).  The CPU oracle is timed on a
 bounded sample of every workload as a reported baseline.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--legs step,c1,...]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--legs step,c1,...]
 """
 import argparse
 import hashlib
@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+WARM_MS = 200.0             # wall time of untimed calls before each leg apart from the step
 PREFILL = "mha_causal_b4_h16_n4096_d128"
 DECODE = "paged_decode_b64_hq32_hkv8_d128"
 NONCAUSAL = "mha_noncausal_b1_h4_n512_d64"
@@ -200,7 +201,7 @@ def write_traffic(runs, copy_mib, commands):
     return 0
 
 
-def time_backward(ea, pc, out, lse, stream, torch, digest, reps=10):
+def time_backward(ea, pc, out, lse, stream, torch, digest, reps=20):
     """attn_bwd on the prefill workload, timed apart from the step.
 
     Gradients are a widening of the path (not part of the step above).  FLOPs
@@ -213,8 +214,7 @@ def time_backward(ea, pc, out, lse, stream, torch, digest, reps=10):
     ws = torch.empty(ea.attn_bwd_workspace_bytes(total_q, pc["Hq"]), dtype=torch.uint8, device=pc["q"].device)
     dq, dk, dv = (torch.empty_like(pc[x]) for x in "qkv")
     kw = dict(causal=pc["causal"], softmax_scale=pc["scale"], dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
-    for _ in range(3):
-        ea.attn_bwd(pc["q"], pc["k"], pc["v"], out, lse, dout, **kw)
+    warm_up(lambda: ea.attn_bwd(pc["q"], pc["k"], pc["v"], out, lse, dout, **kw), torch)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
     for e in ev:
         e[0].record(stream)
@@ -274,8 +274,7 @@ def time_decode_kvcache(ea, W, dev, props, stream, torch, digest, reps=20):
                                max_seqlen_k=max(lens), softmax_scale=c["d"] ** -0.5, rotary_cos=cos,
                                rotary_sin=sin, chunk_tokens=chunk, stream=stream, **bufs)
 
-    for _ in range(3):
-        run()
+    warm_up(run, torch)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
     for e in ev:
         e[0].record(stream)
@@ -318,9 +317,7 @@ def time_fp8(ea, W, pc, stream, torch, digest, reps=20):
         ea.attn_fwd_fp8(qc, kc, vc, qs, ks, vs, causal=pc["causal"], softmax_scale=pc["scale"], incoherent=True,
                         out=out, lse=lse, stream=stream)
 
-    for _ in range(3):
-        quant()
-        attn()
+    warm_up(lambda: (quant(), attn()), torch)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
     for e in ev:
         e[0].record(stream)
@@ -536,10 +533,26 @@ def varlen_bytes(case):
     return 2 * (2 * tq * case["Hq"] * case["d"] + 2 * tk * case["Hkv"] * case["d"]) + 4 * case["Hq"] * tq
 
 
-def time_launches(fn, stream, torch, reps, warm=3):
-    """Per-launch times (ms) of fn, each bracketed by events on `stream`."""
-    for _ in range(warm):
-        fn()
+def warm_up(fn, torch, min_ms=WARM_MS):
+    """Call fn until at least min_ms of wall time has passed (synchronising
+    every few calls): the GPU's clocks settle over tens of milliseconds of
+    work, so a leg that ran only a few warm-up calls would be timed on a
+    clock still ramping up."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms or n >= 4000:
+            return n
+
+
+def time_launches(fn, stream, torch, reps):
+    """Per-launch times (ms) of fn, each bracketed by events on `stream`,
+    after warm_up."""
+    warm_up(fn, torch)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
     for e in ev:
         e[0].record(stream)
@@ -580,7 +593,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--legs", default=",".join(LEGS),
                     help=f"comma-separated legs to run (default: all of {','.join(LEGS)}); "
                          "the headline value needs 'step'")
