@@ -710,6 +710,7 @@ def main():
             step(events[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        step_peak = torch.cuda.max_memory_allocated(dev)
         pre = [e[0].elapsed_time(e[1]) for e in events]
         spl = [e[1].elapsed_time(e[2]) for e in events]
         cmb = [e[2].elapsed_time(e[3]) for e in events]
@@ -724,6 +725,7 @@ def main():
         rec.update({
             "value": round(tflops, 2),
             "ms_per_step": round(wall * 1e3 / args.steps, 4),
+            "peak_device_memory_bytes_step": step_peak,
             "config": {"workload": PREFILL, "B": pc["B"], "Hq": pc["Hq"], "Hkv": pc["Hkv"],
                        "Nq": pc["Nq"], "Nk": pc["Nk"], "d": pc["d"], "causal": pc["causal"],
                        "decode_workload": DECODE, "decode_chunk_tokens": chunk,
@@ -815,6 +817,7 @@ def main():
         rec["fp8_forward"] = fp8
     if cpu and "step" in legs:
         rec["cpu_baseline"] = cpu_baseline_dense(pc, PREFILL, budget_s=12.0)
+    rec["peak_device_memory_bytes"] = torch.cuda.max_memory_allocated(dev)
     print(json.dumps(rec), flush=True)
     return 0
 
