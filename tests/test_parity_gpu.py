@@ -322,3 +322,18 @@ def test_extreme_scale_and_constant_rows():
     assert (got - mean_v[:, None, :, :]).abs().max().item() <= OUT_MAX_ABS
     ql = (c["q"].double() * k1[:, :1].double()).sum(-1) * 0.125  # [B, Nq, Hq]
     assert (lse.to("cpu").double() - (ql.permute(0, 2, 1) + math.log(700))).abs().max().item() <= LSE_ABS
+
+
+@pytest.mark.parametrize("n_seqs", [64, 65, 150])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_many_sequences(n_seqs, d):
+    """Packed batches at and past the size for which the kernel ranks its work items
+    by sequence length (64 sequences); lengths include empty and one-token
+    sequences, Nq > Nk and multi-tile queries. Every element is compared."""
+    rng = np.random.default_rng(7000 + n_seqs + d)
+    nk = [int(x) for x in rng.integers(0, 300, size=n_seqs)]
+    nq = [min(int(x), 300) for x in rng.integers(0, 320, size=n_seqs)]
+    nk[0], nq[0] = 0, 5        # rows with no keys
+    nk[1], nq[1] = 1, 1
+    nk[-1], nq[-1] = 299, 299  # several 128- or 256-row query tiles
+    varlen_parity(nq, nk, 8, 2, d, True, seed=7100 + n_seqs + d)

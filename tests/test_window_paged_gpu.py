@@ -125,3 +125,22 @@ def test_window_none_is_bitwise_attn_fwd():
     assert st == 0
     torch.cuda.synchronize()
     assert torch.equal(out, a[0]) and torch.equal(lse, a[1])
+
+
+@pytest.mark.parametrize("n_seqs", [64, 70])
+def test_paged_prefill_many_sequences(n_seqs):
+    """Paged prefill over batches at and past the length-ranking limit (64 sequences)."""
+    rng = np.random.default_rng(900 + n_seqs)
+    nk = [int(x) for x in rng.integers(1, 700, size=n_seqs)]
+    nq = [min(int(x), n) for x, n in zip(rng.integers(0, 200, size=n_seqs), nk)]
+    q, cq, c = paged_prefill_case(nq, nk, 4, 2, 128, seed=950 + n_seqs)
+    scale = 128 ** -0.5
+    dev = {x: c[x].to(DEV) for x in ("k_cache", "v_cache", "block_table", "seqlens_k")}
+    out, lse = ea.attn_fwd_paged(q.to(DEV), dev["k_cache"], dev["v_cache"], dev["block_table"],
+                                 cq.to(DEV), dev["seqlens_k"], max_seqlen_q=max(nq), causal=True,
+                                 softmax_scale=scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.paged_prefill_ref(to64(q), to64(c["k_cache"]), to64(c["v_cache"]),
+                                            c["block_table"].numpy(), cq.numpy(), c["seqlens_k"].numpy(),
+                                            causal=True, softmax_scale=scale)
+    assert_close(to64(out), to64(lse), ref_o, ref_l, f"paged, {n_seqs} sequences")
