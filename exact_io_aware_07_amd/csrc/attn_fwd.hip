@@ -25,6 +25,14 @@
 // Tiles wholly above the causal boundary are never visited ("FlashAttention:
 // Part 1", section 3.5).  K/V tiles are double-buffered in LDS: the global
 // loads of tile t+1 are issued before tile t is computed.
+//
+// Split-key mode (KSPLIT, for launches with few workgroups): the NW waves of a
+// workgroup own the same 32 * QB query rows and take every NW-th key tile,
+// each wave loading its own tiles into its own LDS stages (no barrier in the
+// loop); at the end their (max, sums, O) states are merged exactly as two
+// tiles merge in the online recurrence ("Flash Attention: A Complete
+// Architectural Autopsy", "The Online Softmax Recurrence") and one wave
+// writes the rows.
 
 #include "attn_tile.h"
 #include "attn_launch.h"
@@ -60,13 +68,15 @@ __device__ __forceinline__ char* q_stash() {
     return buf;
 }
 
-template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN, bool PAGED>
+template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN, bool PAGED, bool KSPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdParams p) {
     static_assert(!PAGED || VARLEN, "paged prefill packs its queries");
+    static_assert(!(KSPLIT && PAGED), "split-key mode reads contiguous K/V");
     static_assert(kFwdPage % BC == 0, "key tiles must not straddle pages");
     constexpr int ROWS_W = 32 * QB;
-    constexpr int BR = NW * ROWS_W;
+    constexpr int BR = KSPLIT ? ROWS_W : NW * ROWS_W;  // query rows per workgroup
+    constexpr int TSTEP = KSPLIT ? NW : 1;              // key tiles between a wave's tiles
     constexpr int KB = BC / 32;  // 32-key blocks per tile
     constexpr int DB = D / 32;   // 32-wide d blocks of O^T
     constexpr int KS = D / 16;   // 16-wide d steps of S^T
@@ -81,18 +91,23 @@ void attn_fwd_kernel(FwdParams p) {
     constexpr int DS_PER = (KS * KB + KS_LDS * QB - ATTN_FWD_K_LEAD) / DS_GROUPS;
     static_assert(KS_LDS == 0 || DS_PER * DS_GROUPS == KS * KB + KS_LDS * QB - ATTN_FWD_K_LEAD,
                   "even LDS read schedule");
-    using Tile = KVDirect<D, BC, NW>;
+    // In split-key mode each wave loads whole tiles into stages of its own.
+    using Tile = KVDirect<D, BC, KSPLIT ? 1 : NW>;
+    constexpr uint32_t STAGE_BYTES = KSPLIT ? NW * Tile::BYTES : Tile::BYTES;
     // Two LDS stages as distinct objects, and a loop unrolled by two so that
     // every access names its stage statically: the compiler can then see that
     // the next tile's LDS-DMA writes never alias the reads of the current
     // tile, and does not wait for them before those reads.
-    __shared__ __attribute__((aligned(1024))) char stage0[Tile::BYTES];
-    __shared__ __attribute__((aligned(1024))) char stage1[Tile::BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
     const int l32 = lane & 31;
+    char* const st0 = stage0 + (KSPLIT ? wave * Tile::BYTES : 0);  // this wave's stages
+    char* const st1 = stage1 + (KSPLIT ? wave * Tile::BYTES : 0);
+    const int lwave = KSPLIT ? 0 : wave;  // the wave's share of a tile's loads
 
     // Work item: heaviest query tiles first (workgroups are dealt to the 8
     // XCDs round-robin, and each XCD runs its share in launch order).
@@ -251,7 +266,7 @@ void attn_fwd_kernel(FwdParams p) {
     const uint16_t* vbase = p.v + ((long)k_off * p.hkv + kvh) * D;
 
     // This wave's rows and the key ranges of its first and last row.
-    const int wr0 = q0 + wave * ROWS_W;
+    const int wr0 = q0 + (KSPLIT ? 0 : wave * ROWS_W);
     const bool wave_rows = wr0 < Nq;
     const int w_last_row = min(wr0 + ROWS_W, Nq) - 1;
     const int w_hi_max = hi_of(w_last_row), w_hi_min = hi_of(wr0);
@@ -269,15 +284,15 @@ void attn_fwd_kernel(FwdParams p) {
             const int phys = __builtin_amdgcn_readfirstlane(phys_v);
             if (phys < 0 || phys >= p.num_pages) {
                 bad = true;
-                Tile::issue(p.k, p.v, stride_b, 0, st, wave, lane);
+                Tile::issue(p.k, p.v, stride_b, 0, st, lwave, lane);
             } else {
                 const long row0 = (long)phys * kFwdPage + key0 % kFwdPage;
                 Tile::issue(p.k + (row0 * p.hkv + kvh) * D, p.v + (row0 * p.hkv + kvh) * D, stride_b,
-                            Nk - key0, st, wave, lane);
+                            Nk - key0, st, lwave, lane);
             }
         } else {
             const long off = (long)key0 * kv_stride;
-            Tile::issue(kbase + off, vbase + off, stride_b, Nk - key0, st, wave, lane);
+            Tile::issue(kbase + off, vbase + off, stride_b, Nk - key0, st, lwave, lane);
         }
     };
 
@@ -326,10 +341,11 @@ void attn_fwd_kernel(FwdParams p) {
     }
     const float c2 = p.scale * kLog2e;
 
+    const int t_first = t_lo + (KSPLIT ? wave : 0);  // this wave's first tile
     int phys_next = 0;  // page id of the next tile to issue (paged mode)
-    if (t_end > t_lo) {
-        issue_tile(t_lo, page_of(t_lo), lds_addr(stage0));
-        if (t_lo + 1 < t_end) phys_next = page_of(t_lo + 1);
+    if (t_first < t_end) {
+        issue_tile(t_first, page_of(t_first), lds_addr(st0));
+        if (t_first + 1 < t_end) phys_next = page_of(t_first + 1);
     }
     wait_vmem();
     __syncthreads();
@@ -337,8 +353,8 @@ void attn_fwd_kernel(FwdParams p) {
     auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
         const char* ks = cur;
         const char* vs = cur + Tile::K_BYTES;
-        if (!ATTN_FWD_SINGLE_STAGE && t + 1 < t_end) {
-            issue_tile(t + 1, phys_next, lds_addr(nxt));
+        if (!ATTN_FWD_SINGLE_STAGE && t + TSTEP < t_end) {
+            issue_tile(t + TSTEP, phys_next, lds_addr(nxt));
             if (PAGED && t + 2 < t_end) phys_next = page_of(t + 2);
         }
         const int k0 = t * BC;
@@ -445,23 +461,74 @@ void attn_fwd_kernel(FwdParams p) {
                         for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(a, pb[kb][qb][c], oacc[db][qb]);
                     }
         }
-        if (ATTN_FWD_SINGLE_STAGE && t + 1 < t_end) {
-            // Check variant: every wave is done with the stage before it is refilled.
-            __syncthreads();
-            issue_tile(t + 1, phys_next, lds_addr(cur));
+        if (ATTN_FWD_SINGLE_STAGE && t + TSTEP < t_end) {
+            // Check variant: every wave is done with the stage before it is
+            // refilled (in split-key mode only this wave reads it).
+            if constexpr (!KSPLIT) __syncthreads();
+            issue_tile(t + TSTEP, phys_next, lds_addr(cur));
             if (PAGED && t + 2 < t_end) phys_next = page_of(t + 2);
         }
         // The next tile's loads (this wave's share) must have landed in LDS
-        // before the barrier releases other waves to read them.
+        // before the barrier releases other waves to read them.  In split-key
+        // mode the waves run different numbers of tiles and share no stage,
+        // so there is no barrier in the loop.
         wait_vmem();
-        __syncthreads();
+        if constexpr (!KSPLIT) __syncthreads();
     };
     if constexpr (ATTN_FWD_SINGLE_STAGE) {
-        for (int t = t_lo; t < t_end; ++t) step(t, stage0, stage0);
+        for (int t = t_first; t < t_end; t += TSTEP) step(t, st0, st0);
     } else {
-        for (int t = t_lo; t < t_end; t += 2) {
-            step(t, stage0, stage1);
-            if (t + 1 < t_end) step(t + 1, stage1, stage0);
+        for (int t = t_first; t < t_end; t += 2 * TSTEP) {
+            step(t, st0, st1);
+            if (t + TSTEP < t_end) step(t + TSTEP, st1, st0);
+        }
+    }
+
+    if constexpr (KSPLIT) {
+        // Merge the waves' states into wave 0: m = max of the shifts, each
+        // wave's sums and O scaled by exp2(m_w - m).  The per-lane layout is
+        // the same in every wave (same rows), so the merge is lane-wise.
+        // Layout in stage0: [wave - 1][item][lane] floats, item = per qb
+        // (m, l, lr, O^T registers).
+        constexpr int ITEMS = QB * (3 + DB * 16);
+        static_assert((NW - 1) * ITEMS * 64 * 4 <= STAGE_BYTES, "merge area fits the stages");
+        float* const xs = reinterpret_cast<float*>(stage0);
+        __syncthreads();  // every wave is done with its stages
+        if (wave > 0) {
+            float* w = xs + (wave - 1) * ITEMS * 64 + lane;
+            int k = 0;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                w[64 * k++] = m_run[qb];
+                w[64 * k++] = l_part[qb];
+                w[64 * k++] = lr_part[qb];
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) w[64 * k++] = oacc[db][qb][r];
+            }
+        }
+        __syncthreads();
+        if (wave > 0) return;
+        for (int ow = 1; ow < NW; ++ow) {
+            const float* w = xs + (ow - 1) * ITEMS * 64 + lane;
+            int k = 0;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mo = w[64 * k++];
+                const float lo = w[64 * k++];
+                const float lro = w[64 * k++];
+                const float m = fmaxf(m_run[qb], mo);
+                const float a = m_run[qb] == -INFINITY ? 0.0f : exp2f(m_run[qb] - m);
+                const float bs = mo == -INFINITY ? 0.0f : exp2f(mo - m);
+                l_part[qb] = l_part[qb] * a + lo * bs;
+                lr_part[qb] = lr_part[qb] * a + lro * bs;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][qb][r] = oacc[db][qb][r] * a + w[64 * k++] * bs;
+                m_run[qb] = m;
+            }
         }
     }
 
@@ -495,15 +562,15 @@ void attn_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN, bool PAGED>
+template <int D, int QB, int BC, int NW, int WPE, bool CAUSAL, bool VARLEN, bool PAGED, bool KSPLIT = false>
 static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     FwdParams p = p0;
-    constexpr int BR = NW * 32 * QB;
+    constexpr int BR = KSPLIT ? 32 * QB : NW * 32 * QB;
     p.n_qtiles = (p.max_q + BR - 1) / BR;
     const long grid = (long)p.n_qtiles * p.batch * p.hq;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, WPE, CAUSAL, VARLEN, PAGED>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, WPE, CAUSAL, VARLEN, PAGED, KSPLIT>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
@@ -541,10 +608,32 @@ static hipError_t launch_fwd_d(const FwdParams& p, bool causal, bool varlen, boo
 #define ATTN_FWD256_CFG 1, 32, 8, 2
 #endif
 
+// Split-key mode: four waves share 32 query rows, each with its own stages.
+template <int D, int BC>
+static hipError_t launch_fwd_split(const FwdParams& p, bool causal, bool varlen, hipStream_t s) {
+    if (causal)
+        return varlen ? launch_fwd_cfg<D, 1, BC, 4, 2, true, true, false, true>(p, s)
+                      : launch_fwd_cfg<D, 1, BC, 4, 2, true, false, false, true>(p, s);
+    return varlen ? launch_fwd_cfg<D, 1, BC, 4, 2, false, true, false, true>(p, s)
+                  : launch_fwd_cfg<D, 1, BC, 4, 2, false, false, false, true>(p, s);
+}
+
+// A launch whose usual grid (workgroups of `rows` query rows) fills at most
+// half of the 256 compute units, with at least eight key tiles of `bc` keys
+// per row and no narrow window, runs in split-key mode: four times the
+// workgroups, each wave walking a quarter of the keys.
+static bool use_split(const FwdParams& p, int rows, int bc) {
+    const long grid = (long)((p.max_q + rows - 1) / rows) * p.batch * p.hq;
+    return grid <= 128 && p.max_k >= 8 * bc && (p.wl < 0 || p.wl >= 8 * bc);
+}
+
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, bool paged, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_fwd_d<64, ATTN_FWD64_CFG>(p, causal, varlen, paged, s);
+        case 64:
+            if (!paged && use_split(p, 128, 64)) return launch_fwd_split<64, 64>(p, causal, varlen, s);
+            return launch_fwd_d<64, ATTN_FWD64_CFG>(p, causal, varlen, paged, s);
         case 128:
+            if (!paged && use_split(p, 256, 32)) return launch_fwd_split<128, 32>(p, causal, varlen, s);
             // A narrow left window uses w + 1 of the 256 + w keys a 256-row
             // tile streams; 128-row workgroups waste half as much (measured
             // on the 4096-token causal workload: +14% at w = 512, +25% at

@@ -337,3 +337,45 @@ def test_varlen_many_sequences(n_seqs, d):
     nk[1], nq[1] = 1, 1
     nk[-1], nq[-1] = 299, 299  # several 128- or 256-row query tiles
     varlen_parity(nq, nk, 8, 2, d, True, seed=7100 + n_seqs + d)
+
+
+# Launches whose usual grid has at most 128 workgroups (256 query rows per
+# workgroup at d = 128, 128 at d = 64) and at least 8 key tiles (256 keys at
+# d = 128, 512 at d = 64) run in split-key mode: four waves share 32 query
+# rows and each walks a quarter of the keys, then their states are merged.
+SPLIT_DENSE = [
+    # (B, Nq, Nk, Hq, Hkv, d, causal, window)
+    (1, 2048, 2048, 4, 4, 64, True, (-1, -1)),
+    (2, 128, 8192, 16, 4, 128, True, (-1, -1)),
+    (1, 64, 16384, 32, 8, 128, True, (-1, -1)),
+    (1, 300, 1000, 8, 1, 128, False, (-1, -1)),   # ragged tiles, MQA
+    (1, 1000, 600, 4, 2, 64, True, (-1, -1)),     # Nq > Nk: rows with no keys
+    (1, 512, 4096, 4, 4, 128, True, (300, -1)),   # a window wider than 8 tiles
+    (3, 33, 777, 2, 2, 128, False, (-1, -1)),     # one short query tile per sequence
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_DENSE, ids=lambda s: "x".join(map(str, s[:7])))
+def test_split_key_mode_dense(shape):
+    B, Nq, Nk, Hq, Hkv, d, causal, window = shape
+    case = W.dense_case(B, Nq, Nk, Hq, Hkv, d, seed=8000 + Nq + d, device=DEV)
+    out, lse = ea.attn_fwd(case["q"], case["k"], case["v"], causal=causal, softmax_scale=d ** -0.5,
+                           window=window)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention_ref(to64(case["q"]), to64(case["k"]), to64(case["v"]), causal=causal,
+                                        softmax_scale=d ** -0.5, window=window)
+    o = to64(out)
+    empty = np.isneginf(ref_l)
+    if empty.any():
+        bb, hh, ii = np.nonzero(empty)
+        assert np.all(o[bb, ii, hh] == 0)
+    assert_close(o, to64(lse), ref_o, ref_l, f"split-key {shape}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_split_key_mode_varlen(d):
+    """Packed batches with a small grid: one long-context chunk, an empty sequence, a short one."""
+    nq = [200, 0, 17, 3]
+    nk = [5000, 700, 17, 900]
+    varlen_parity(nq, nk, 8, 2, d, True, seed=8100 + d)
+    varlen_parity([150], [4000], 4, 4, d, False, seed=8200 + d)

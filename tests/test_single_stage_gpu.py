@@ -46,11 +46,16 @@ def both(fn):
 
 DENSE = [
     # (B, Nq, Nk, Hq, Hkv, d, causal, window)
+    # Grids of at most 128 workgroups with enough keys run in split-key mode
+    # (each wave its own stages): the first three.
     (2, 1024, 1024, 4, 4, 128, True, (-1, -1)),
     (1, 700, 1500, 8, 2, 128, True, (-1, -1)),
     (1, 513, 777, 4, 1, 64, False, (-1, -1)),
+    # Shared stages: d = 256, a narrow window, and grids over 128 workgroups.
     (1, 600, 600, 4, 2, 256, True, (-1, -1)),
     (1, 1024, 1024, 4, 2, 128, True, (255, -1)),
+    (2, 2048, 2048, 16, 4, 128, True, (-1, -1)),
+    (2, 1024, 1030, 16, 16, 64, False, (-1, -1)),
 ]
 
 
