@@ -14,6 +14,7 @@ raises.
     out, lse = attn_decode_combine(part_o, part_l, seqlens_k, chunk_tokens=c)
     dq, dk, dv = attn_bwd(q, k, v, out, lse, dout, causal=True, softmax_scale=s)
 """
+import contextlib
 import ctypes
 import os
 
@@ -117,6 +118,13 @@ def _stream(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(dev):
+    """Make dev the current device for a call (a no-op context when it already is)."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
+
+
 def _need(t, name, dtype, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -188,7 +196,7 @@ def attn_fwd(q, k, v, *, causal, softmax_scale, cu_seqlens_q=None, cu_seqlens_k=
     if q.numel() == 0:
         return out, lse
     wl, wr = (int(x) for x in window)
-    with torch.cuda.device(dev):
+    with _on(dev):
         if wl == -1 and wr == -1:
             st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                 batch, mq, mk, hq, hkv, d, 1 if causal else 0, float(softmax_scale),
@@ -231,7 +239,7 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seqlens_k, *,
     if tq == 0:
         return out, lse
     wl, wr = (int(x) for x in window)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_fwd_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q), None,
                                _ptr(block_table), _ptr(seqlens_k), batch, int(max_seqlen_q), 0, hq, hkv,
                                d, page, block_table.shape[1], num_pages, 1 if causal else 0, wl, wr,
@@ -300,7 +308,7 @@ def attn_bwd(q, k, v, out, lse, dout, *, causal, softmax_scale, cu_seqlens_q=Non
         _need(workspace, "workspace", torch.uint8, dev)
     if q.numel() == 0:
         return dq, dk, dv
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
                             _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, mq, mk, total_q, hq, hkv,
                             d, 1 if causal else 0, float(softmax_scale), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -348,7 +356,7 @@ def attn_decode_splitkv(q, k_cache, v_cache, block_table, seqlens_k, *, chunk_to
     _need(lse_partial, "lse_partial", torch.float32, dev)
     if out_partial.numel() < n * batch * hq * d or lse_partial.numel() < n * batch * hq:
         raise ValueError("partial buffers are too small for num_splits")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_decode_splitkv(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                        _ptr(seqlens_k), batch, hq, hkv, d, page,
                                        block_table.shape[1], num_pages, int(chunk_tokens), n,
@@ -377,7 +385,7 @@ def attn_decode_combine(out_partial, lse_partial, seqlens_k, *, chunk_tokens, ou
         lse = None
     if lse is not None:
         _need(lse, "lse", torch.float32, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_decode_combine(_ptr(out_partial), _ptr(lse_partial), _ptr(seqlens_k), batch,
                                        hq, d, int(chunk_tokens), n, _ptr(out), _ptr(lse),
                                        _stream(stream, dev))
@@ -427,7 +435,7 @@ def attn_decode_noalloc(q, k_cache, v_cache, block_table, seqlens_k, *, max_seql
         lse = None
     if lse is not None:
         _need(lse, "lse", torch.float32, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                        _ptr(seqlens_k), batch, hq, hkv, d, page, block_table.shape[1],
                                        num_pages, int(chunk_tokens), n, float(softmax_scale), _ptr(out),
@@ -501,7 +509,7 @@ def attn_decode_kvcache(q, k_new, v_new, k_cache, v_cache, block_table, seqlens_
         lse = None
     if lse is not None:
         _need(lse, "lse", torch.float32, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_decode_kvcache(
             _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
             _ptr(seqlens_k), _ptr(rotary_cos), _ptr(rotary_sin), rot, int(bool(rotary_interleaved)),
@@ -542,7 +550,7 @@ def attn_fp8_quantize(x, *, signs=None, layout="rows", codes=None, scales=None, 
         _need(signs, "signs", torch.int8, dev)
         if tuple(signs.shape) != (d,):
             raise ValueError("signs must be [head_dim]")
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_fp8_quantize(_ptr(x), _ptr(signs), B, N, H, d, lay, _ptr(codes), _ptr(scales),
                                      _stream(stream, dev))
     _check(st)
@@ -577,7 +585,7 @@ def attn_fwd_fp8(q_codes, k_codes, v_codes_t, q_scales, k_scales, v_scales, *, c
         lse = None
     if lse is not None:
         _need(lse, "lse", torch.float32, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_fwd_fp8(_ptr(q_codes), _ptr(k_codes), _ptr(v_codes_t), _ptr(q_scales), _ptr(k_scales),
                                 _ptr(v_scales), B, Nq, Nk, Hq, Hkv, d, int(bool(causal)), int(bool(incoherent)),
                                 float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream, dev))
@@ -604,7 +612,7 @@ def ceiling_read(src, sink=None, stream=None):
     if sink is None:
         sink = torch.empty(lib().attn_ceiling_read_sink_words(src.numel() * src.element_size()), dtype=torch.int32,
                            device=dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().attn_ceiling_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, lib().attn_ceiling_last_error().decode())
@@ -619,7 +627,7 @@ def _ceiling_mfma(fn, words, operands, iters, sink, stream):
         raise ValueError(f"operands must be [waves, 64, {words}]")
     if sink is None:
         sink = torch.empty(waves * 64, dtype=torch.float32, device=dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = fn(_ptr(operands), waves, int(iters), _ptr(sink), _stream(stream, dev))
     if st != 0:
         raise AttnError(st, lib().attn_ceiling_last_error().decode())
