@@ -5,10 +5,10 @@ on purpose" (the tests there bound the error by twice the error of a
 lower-precision PyTorch reference against a higher-precision path, with an
 extra absolute allowance): for each of dq, dk and dv,
 
-    max |gpu - oracle|  <= 2 * max |bf16 reference - oracle|  + 1e-3 * max |oracle|
-    mean |gpu - oracle| <= 2 * mean |bf16 reference - oracle| + 1e-4 * max |oracle|
+    max |gpu - oracle|  <= 2 * max |bf16 reference - oracle|  + 1e-3 * G
+    mean |gpu - oracle| <= 2 * mean |bf16 reference - oracle| + 1e-4 * G
 
-where the bf16 reference is plain PyTorch autograd on the CPU over the same
+with G the largest |oracle| over dq, dk and dv together, where the bf16 reference is plain PyTorch autograd on the CPU over the same
 bf16 inputs with every tensor kept in bf16 (scores, probabilities, output),
 and the oracle is oracle.attention_bwd_ref in fp64.
 """
@@ -72,13 +72,20 @@ def bf16_reference(q, k, v, dout, *, causal, scale, cu_q=None, cu_k=None, heads=
 
 
 def assert_grads(gpu, ref, low, tag, mask=None):
+    # The absolute allowance is taken relative to the largest reference
+    # gradient of the problem (dq, dk and dv together): a gradient that is
+    # exactly zero (a row with a single visible key has dS = P (dP - D) = 0)
+    # still leaves room for the fp32 rounding of dP - D.
+    sel = []
     for name, g, r, lo in zip(("dq", "dk", "dv"), gpu, ref, low):
         if mask is not None:
             g, r, lo = g[mask[name]], r[mask[name]], lo[mask[name]]
+        sel.append((name, g, r, lo))
+    scale = max([np.max(np.abs(r)) for _, _, r, _ in sel if r.size] + [1e-30])
+    for name, g, r, lo in sel:
         if r.size == 0:
             continue
         assert np.all(np.isfinite(g)), f"{tag} {name}: non-finite"
-        scale = max(np.max(np.abs(r)), 1e-30)
         e_gpu, e_low = np.abs(g - r), np.abs(lo - r)
         assert e_gpu.max() <= 2 * e_low.max() + 1e-3 * scale, (
             f"{tag} {name}: max err {e_gpu.max():.3e} vs bf16 reference {e_low.max():.3e} (scale {scale:.3e})")
@@ -175,3 +182,11 @@ def test_bwd_deterministic():
     b = run_dense(1, 256, 384, 4, 2, 128, True, seed=5)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_bwd_single_visible_key():
+    """Nq > Nk with one key: only the last rows see it, each row has a single
+    visible key, so dS = P (dP - D) vanishes and dq is exactly zero in exact
+    arithmetic (the allowance then comes from dk and dv's scale)."""
+    run_dense(2, 52, 1, 8, 2, 128, True, seed=130)
+    run_dense(1, 40, 3, 4, 4, 64, True, seed=131)
