@@ -381,10 +381,15 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         if (it + 1 < n_it) step(it + 1, stage1, stage0);
     }
 
-    if (key < Nk) {
-        const long off = ((long)(k_off + key) * p.hkv + kvh) * D;
-        store_rows_bf16<DB>(p.dk + off, dk, p.scale, lane);
-        store_rows_bf16<DB>(p.dv + off, dv, 1.0f, lane);
+    {
+        // dK then dV rows through the wave's own LDS region (the stages are
+        // free after the last barrier): 16-byte stores of whole rows.
+        constexpr uint32_t WB = 32u * D * 2;
+        static_assert((NW / 2) * WB <= STAGE, "output staging fits the stages");
+        char* const ob = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * WB;
+        const long off = ((long)(k_off + kw0) * p.hkv + kvh) * D;
+        store_rows_bf16_staged<DB>(ob, dk, p.scale, lane, p.dk + off, (long)p.hkv * D, Nk - kw0);
+        store_rows_bf16_staged<DB>(ob, dv, 1.0f, lane, p.dv + off, (long)p.hkv * D, Nk - kw0);
     }
 }
 
@@ -666,12 +671,16 @@ void attn_bwd_dkdv_pair_kernel(BwdParams p) {
         }
     }
 
-    if (key < Nk) {
-        const long off = ((long)(k_off + key) * p.hkv + kvh) * D;
-        if (side_p)
-            store_rows_bf16<DB>(p.dv + off, acc, 1.0f, lane);
-        else
-            store_rows_bf16<DB>(p.dk + off, acc, p.scale, lane);
+    // dV (P side) or dK (dS side) rows through LDS: the dS side's last dK
+    // products may still read a stage, so every wave first passes a barrier.
+    __syncthreads();
+    {
+        constexpr uint32_t WB = 32u * D * 2;
+        static_assert((NW / 2) * WB <= STAGE, "output staging fits the stages");
+        char* const ob = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * WB;
+        const long off = ((long)(k_off + kw0) * p.hkv + kvh) * D;
+        store_rows_bf16_staged<DB>(ob, acc, side_p ? 1.0f : p.scale, lane, (side_p ? p.dv : p.dk) + off,
+                                   (long)p.hkv * D, Nk - kw0);
     }
 }
 
@@ -838,7 +847,15 @@ void attn_bwd_dq_kernel(BwdParams p) {
         if (t + 1 < n_tiles) step(t + 1, stage1, stage0);
     }
 
-    if (row < Nq) store_rows_bf16<DB>(p.dq + ((long)(q_off + row) * p.hq + hq) * D, dacc, p.scale, lane);
+    {
+        // dQ rows through LDS (the wave's own region of the stages, free after
+        // the last barrier): 16-byte stores of whole rows.
+        constexpr uint32_t WB = 32u * D * 2;
+        static_assert((NW / 2) * WB <= Tile::BYTES, "output staging fits the stages");
+        char* const ob = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * WB;
+        store_rows_bf16_staged<DB>(ob, dacc, p.scale, lane, p.dq + ((long)(q_off + wr0) * p.hq + hq) * D,
+                                   (long)p.hq * D, Nq - wr0);
+    }
 }
 
 // ---- launchers -------------------------------------------------------------------

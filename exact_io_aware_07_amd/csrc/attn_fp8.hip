@@ -505,6 +505,18 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     }
 
     const float l_tot = pair_sum(l_part);
+    constexpr uint32_t WB = 32u * D * 2;  // a wave's output rows in bf16
+    if constexpr ((NW / 2) * WB <= STAGE) {
+        // Output rows through LDS (the wave's own region of the stages, free
+        // after the last barrier): 16-byte stores of whole rows.
+        char* const ob = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * WB;
+        const float inv = l_tot > 0.0f ? vref / (exp2f(kFp8PScale) * l_tot) : 0.0f;
+        store_rows_bf16_staged<DBD>(ob, oacc, inv, lane, p.out + (((long)b * Nq + wr0) * p.hq + hq) * D,
+                                    (long)p.hq * D, Nq - wr0);
+        if (row < Nq && p.lse != nullptr && h == 0)
+            p.lse[((long)b * p.hq + hq) * Nq + row] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+        return;
+    }
     if (row < Nq) {
         const float inv = l_tot > 0.0f ? vref / (exp2f(kFp8PScale) * l_tot) : 0.0f;
         uint16_t* orow = p.out + (((long)b * Nq + row) * p.hq + hq) * D;

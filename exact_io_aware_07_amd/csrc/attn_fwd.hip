@@ -536,34 +536,20 @@ void attn_fwd_kernel(FwdParams p) {
     const int h = lane >> 5;
     const int total_q = VARLEN ? p.cu_q[p.batch] : 0;
     if constexpr (D <= 128 && !KSPLIT && QB == 1) {
-        // The wave's 32 output rows go through LDS (its own region of the
-        // stages, free after the last barrier) so that each global store
-        // writes 16 whole bytes per lane and 16 lanes write a whole row.
-        constexpr int CHR = D / 8;                 // 16-byte chunks per row
-        constexpr uint32_t WB = 32u * D * 2;       // bytes per wave
+        // Output rows through LDS (the wave's own region of the stages, free
+        // after the last barrier): 16-byte stores of whole rows.
+        constexpr uint32_t WB = 32u * D * 2;  // bytes per wave
         static_assert((NW / 2) * WB <= STAGE_BYTES, "output staging fits the stages");
         char* const ob = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * WB;
         const int row = wr0 + l32;
         const float l_tot = pair_sum(l_part[0]);
         const float lr_tot = pair_sum(lr_part[0]);
         const float inv = bad ? NAN : (l_tot > 0.0f ? 1.0f / lr_tot : 0.0f);
+        f32x16 oq[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w = {pack_bf16x2(oacc[db][0][4 * g] * inv, oacc[db][0][4 * g + 1] * inv),
-                           pack_bf16x2(oacc[db][0][4 * g + 2] * inv, oacc[db][0][4 * g + 3] * inv)};
-                const int ch = 4 * db + g;
-                *reinterpret_cast<u32x2*>(ob + l32 * (D * 2) + ((ch ^ (l32 & (CHR - 1))) * 16) + h * 8) = w;
-            }
-        constexpr int RPP = 1024 / (D * 2);        // rows per 64-lane pass
-#pragma unroll
-        for (int i = 0; i < 32 / RPP; ++i) {
-            const int r = i * RPP + lane / CHR, c = lane % CHR;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ob + r * (D * 2) + ((c ^ (r & (CHR - 1))) * 16));
-            if (wr0 + r < Nq)
-                *reinterpret_cast<u32x4*>(p.out + ((long)(q_off + wr0 + r) * p.hq + hq) * D + c * 8) = v;
-        }
+        for (int db = 0; db < DB; ++db) oq[db] = oacc[db][0];
+        store_rows_bf16_staged<DB>(ob, oq, inv, lane, p.out + ((long)(q_off + wr0) * p.hq + hq) * D,
+                                   (long)p.hq * D, Nq - wr0);
         if (row < Nq && p.lse != nullptr && h == 0) {
             const float lse = bad ? NAN : (l_tot > 0.0f ? (m_run[0] + __log2f(l_tot)) * kLn2 : -INFINITY);
             if constexpr (VARLEN)

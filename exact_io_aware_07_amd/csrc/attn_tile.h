@@ -311,4 +311,37 @@ __device__ __forceinline__ u32x4 read_vt16_tr(const char* vs, int db, int lane) 
     return u32x4{w1[0], w1[1], w2[0], w2[1]};
 }
 
+// ---- output rows through LDS ------------------------------------------------
+// A wave's 32 rows of a 32x32 accumulator set (lane l holds row l % 32, d
+// values 32 db + 8 g + 4 (l / 32) .. + 3 in acc[db][4 g .. 4 g + 3]) scaled by
+// mul (per lane, so per row), rounded to bf16 and written to rows [0, nrows)
+// of dst (row r at dst + r * stride elements).  The rows go through the wave's
+// own LDS region `ob` (32 * 64 * DB bytes; 16-byte chunks XOR-swizzled by
+// row) so that each global store writes 16 bytes per lane and a group of
+// lanes writes whole rows, instead of 8-byte pieces scattered over 32 rows.
+// The caller makes sure no other wave still reads `ob`.
+template <int DB>
+__device__ __forceinline__ void store_rows_bf16_staged(char* ob, const f32x16 (&acc)[DB], float mul, int lane,
+                                                       uint16_t* dst, long stride, int nrows) {
+    constexpr int D = 32 * DB;
+    constexpr int CHR = D / 8;          // 16-byte chunks per row
+    constexpr int RPP = 1024 / (D * 2); // rows per 64-lane pass
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x2 w = {pack_bf16x2(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                             pack_bf16x2(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+            const int ch = 4 * db + g;
+            *reinterpret_cast<u32x2*>(ob + l32 * (D * 2) + ((ch ^ (l32 & (CHR - 1))) * 16) + h * 8) = w;
+        }
+#pragma unroll
+    for (int i = 0; i < 32 / RPP; ++i) {
+        const int r = i * RPP + lane / CHR, c = lane % CHR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ob + r * (D * 2) + ((c ^ (r & (CHR - 1))) * 16));
+        if (r < nrows) *reinterpret_cast<u32x4*>(dst + (long)r * stride + c * 8) = v;
+    }
+}
+
 }  // namespace attn
