@@ -308,42 +308,18 @@ void attn_fwd_kernel(FwdParams p) {
         }
         return qf[qb][s < KS_REG ? s : 0];
     };
-    // Where the LDS budget of the workgroups a CU holds leaves room, the
-    // wave's Q rows take a detour through LDS: whole-row loads (16 lanes per
-    // row, as for a key tile) into a slot laid out like a K stage, read back
-    // as fragments once the stage below has landed.  Loading the fragments
-    // directly touches 32 rows per instruction, 32 bytes of each.
-    constexpr int WG_PER_CU = 4 * WPE / NW > 0 ? 4 * WPE / NW : 1;
-    constexpr bool Q_VIA_LDS =
-        !KSPLIT && KS_LDS == 0 && (2 * STAGE_BYTES + NW * ROWS_W * D * 2) * WG_PER_CU <= 156 * 1024;
-    char* qslot = nullptr;
-    if constexpr (Q_VIA_LDS) {
-        constexpr int CH = D / 8, RPI = 1024 / (2 * D), NI = ROWS_W * 2 * D / 1024;
-        qslot = q_stash<NW * ROWS_W * D * 2>() + wave * (ROWS_W * D * 2);
-        const int nv = Nq - wr0;
-        const uint32_t stride_b = (uint32_t)p.hq * D * 2;
-        const u32x4 rq = rsrc_words(p.q + ((long)(q_off + wr0) * p.hq + hq) * D,
-                                    nv > 0 ? (uint32_t)(nv < ROWS_W ? nv : ROWS_W) * stride_b : 0u);
-        const uint32_t qs_addr = lds_addr(qslot);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const uint32_t row = i * RPI + lane / CH, pc = lane % CH;
-            dma16(rq, qs_addr + i * 1024, row * stride_b + ((pc ^ swz<CH>(row)) * 16));
-        }
-    } else {
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = wr0 + 32 * qb + l32;
+        const uint16_t* qrow = p.q + ((long)(q_off + row) * p.hq + hq) * D;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int row = wr0 + 32 * qb + l32;
-            const uint16_t* qrow = p.q + ((long)(q_off + row) * p.hq + hq) * D;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if (row < Nq) z = load16(qrow + (2 * s + (lane >> 5)) * 8);
-                if (s < KS_REG)
-                    qf[qb][s < KS_REG ? s : 0] = z;
-                else if constexpr (KS_LDS > 0)
-                    *reinterpret_cast<u32x4*>(qlds + (qb * KS_LDS + s - KS_REG) * 1024) = z;
-            }
+        for (int s = 0; s < KS; ++s) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (row < Nq) z = load16(qrow + (2 * s + (lane >> 5)) * 8);
+            if (s < KS_REG)
+                qf[qb][s < KS_REG ? s : 0] = z;
+            else if constexpr (KS_LDS > 0)
+                *reinterpret_cast<u32x4*>(qlds + (qb * KS_LDS + s - KS_REG) * 1024) = z;
         }
     }
 
@@ -372,16 +348,6 @@ void attn_fwd_kernel(FwdParams p) {
         if (t_first + 1 < t_end) phys_next = page_of(t_first + 1);
     }
     wait_vmem();
-    if constexpr (Q_VIA_LDS) {
-        // The slot holds this wave's own loads, complete after the wait above,
-        // so the fragments are read before the barrier; the empty asm keeps
-        // the compiler from hoisting the reads above the wait.
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) qf[qb][s] = read_k_frag<D>(qslot, qb, s, lane);
-    }
     __syncthreads();
 
     auto step = [&](const int t, char* cur, char* nxt) __attribute__((always_inline)) {
