@@ -123,11 +123,11 @@ void attn_fwd_kernel(FwdParams p) {
         int item;
         if ((p.hq & 7) == 0) {
             const int hpx = p.hq >> 3, x = bid & 7, kk = bid >> 3;
-            item = kk / hpx;
-            hq = x * hpx + kk % hpx;
+            item = (int)udiv_apply(kk, p.dv_hpx);
+            hq = x * hpx + (kk - item * hpx);
         } else {
-            item = bid / p.hq;
-            hq = bid % p.hq;
+            item = (int)udiv_apply(bid, p.dv_bh);
+            hq = bid - item * p.hq;
         }
         if (p.batch <= kLengthOrderMax) {
             // Items run longest sequence first (more keys, ties by index),
@@ -185,8 +185,9 @@ void attn_fwd_kernel(FwdParams p) {
                 qt = (s_first[lo + 1] - s_first[lo]) - 1 - (item - s_first[lo]);
             }
         } else {
-            qt = p.n_qtiles - 1 - item / p.batch;
-            b = item % p.batch;
+            const int ib = (int)udiv_apply(item, p.dv_batch);
+            qt = p.n_qtiles - 1 - ib;
+            b = item - ib * p.batch;
         }
     } else {
         // Equal-length sequences: when the (sequence, head) count is a
@@ -195,16 +196,18 @@ void attn_fwd_kernel(FwdParams p) {
         int bh;
         if ((BH & 7) == 0) {
             const int hpx = BH >> 3, x = bid & 7, kk = bid >> 3;
-            qt = p.n_qtiles - 1 - kk / hpx;
-            bh = x * hpx + kk % hpx;
+            const int kq = (int)udiv_apply(kk, p.dv_hpx);
+            qt = p.n_qtiles - 1 - kq;
+            bh = x * hpx + (kk - kq * hpx);
         } else {
-            qt = p.n_qtiles - 1 - bid / BH;
-            bh = bid % BH;
+            const int kq = (int)udiv_apply(bid, p.dv_bh);
+            qt = p.n_qtiles - 1 - kq;
+            bh = bid - kq * BH;
         }
-        b = bh / p.hq;
-        hq = bh % p.hq;
+        b = (int)udiv_apply(bh, p.dv_hq);
+        hq = bh - b * p.hq;
     }
-    const int kvh = hq / (p.hq / p.hkv);
+    const int kvh = (int)udiv_apply(hq, p.dv_grp);
 
     int q_off, k_off = 0, Nq, Nk;
     bool bad = false;  // paged: a page id out of range, or more keys than the table holds
@@ -591,6 +594,14 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     FwdParams p = p0;
     constexpr int BR = KSPLIT ? 32 * QB : NW * 32 * QB;
     p.n_qtiles = (p.max_q + BR - 1) / BR;
+    // Divisors of the work-item mapping (see attn_udiv.h).
+    const int bh_all = p.batch * p.hq;
+    const int per_xcd = (VARLEN ? p.hq : bh_all) >> 3;
+    p.dv_hpx = udiv_make(per_xcd > 0 ? per_xcd : 1);
+    p.dv_bh = udiv_make(VARLEN ? p.hq : bh_all);
+    p.dv_hq = udiv_make(p.hq);
+    p.dv_batch = udiv_make(p.batch);
+    p.dv_grp = udiv_make(p.hkv > 0 ? p.hq / p.hkv : 1);
     const long grid = (long)p.n_qtiles * p.batch * p.hq;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_udiv.h"
+
 namespace attn {
 
 struct FwdParams {
@@ -22,6 +24,10 @@ struct FwdParams {
     const int32_t* block_table = nullptr;
     const int32_t* seqlens_k = nullptr;
     int max_pages = 0, num_pages = 0;
+    // Divisors of the work-item mapping, filled in by the launcher: query
+    // heads per XCD (dense: (sequence, head) pairs per XCD), heads (dense:
+    // sequences x heads), query heads, sequences, query heads per K/V head.
+    UDiv dv_hpx, dv_bh, dv_hq, dv_batch, dv_grp;
 };
 
 struct DecodeParams {
