@@ -43,7 +43,7 @@ VARLEN = "varlen_chunked_prefill_16seq_hq32_hkv8"
 # Legs: the step (prefill + decode, the headline) and the separately timed ones.
 LEGS = ["step", "c1", "c3", "c4_d128", "c4_d64", "c4_d256", "backward", "kvcache", "fp8", "ceilings"]
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-KERNEL_SOURCES = ["attn_tile.h", "attn_launch.h", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_fp8.hip"]
+KERNEL_SOURCES = ["attn_tile.h", "attn_launch.h", "attn_udiv.h", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "attn_fp8.hip"]
 
 
 def source_digest():
