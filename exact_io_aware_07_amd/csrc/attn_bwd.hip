@@ -217,9 +217,10 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     // Key tiles in ascending order: under a causal mask the first key tiles
     // are seen by the most query rows, so the heaviest work starts first.
     const int BH = p.batch * p.hkv;
-    const int kt = blockIdx.x / BH;
-    const int b = (blockIdx.x % BH) / p.hkv;
-    const int kvh = blockIdx.x % p.hkv;
+    const int kt = (int)udiv_apply(blockIdx.x, p.dv_bh);
+    const int bh = (int)blockIdx.x - kt * BH;
+    const int b = (int)udiv_apply(bh, p.dv_h);
+    const int kvh = bh - b * p.hkv;
     int q_off, k_off, Nq, Nk;
     if constexpr (VARLEN) {
         q_off = p.cu_q[b];
@@ -265,7 +266,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
         }
 
     // Query blocks that see at least one key of this workgroup.
-    const int g = p.hq / p.hkv;
+    const int g = p.grp;
     int qb_lo = 0;
     if constexpr (CAUSAL) {
         const int i_min = j0 - shift;  // first row that sees key j0
@@ -428,9 +429,10 @@ void attn_bwd_dkdv_pair_kernel(BwdParams p) {
     const int l32 = lane & 31;
 
     const int BH = p.batch * p.hkv;
-    const int kt = blockIdx.x / BH;
-    const int b = (blockIdx.x % BH) / p.hkv;
-    const int kvh = blockIdx.x % p.hkv;
+    const int kt = (int)udiv_apply(blockIdx.x, p.dv_bh);
+    const int bh = (int)blockIdx.x - kt * BH;
+    const int b = (int)udiv_apply(bh, p.dv_h);
+    const int kvh = bh - b * p.hkv;
     int q_off, k_off, Nq, Nk;
     if constexpr (VARLEN) {
         q_off = p.cu_q[b];
@@ -469,7 +471,7 @@ void attn_bwd_dkdv_pair_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-    const int g = p.hq / p.hkv;
+    const int g = p.grp;
     int qb_lo = 0;
     if constexpr (CAUSAL) {
         const int i_min = j0 - shift;
@@ -707,10 +709,12 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
     // Heaviest query tiles first.
     const int BH = p.batch * p.hq;
-    const int qt = p.n_tiles - 1 - (int)(blockIdx.x / BH);
-    const int b = (blockIdx.x % BH) / p.hq;
-    const int hq = blockIdx.x % p.hq;
-    const int kvh = hq / (p.hq / p.hkv);
+    const int qq = (int)udiv_apply(blockIdx.x, p.dv_bh);
+    const int qt = p.n_tiles - 1 - qq;
+    const int bh = (int)blockIdx.x - qq * BH;
+    const int b = (int)udiv_apply(bh, p.dv_h);
+    const int hq = bh - b * p.hq;
+    const int kvh = (int)udiv_apply(hq, p.dv_grp);
     int q_off, k_off, Nq, Nk;
     if constexpr (VARLEN) {
         q_off = p.cu_q[b];
@@ -868,6 +872,8 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
     // 32-row wave take a SIMD's budget, so 4 waves at one per SIMD.
     constexpr int DQ_NW = D == 256 ? 4 : 8, DQ_WPE = D == 256 ? 1 : 2;
     BwdParams p = p0;
+    p.grp = p.hkv > 0 ? p.hq / p.hkv : 1;
+    p.dv_grp = udiv_make(p.grp);
     {
         const long waves = ((long)p.total_q + 15) / 16 * p.hq;  // 16 rows of one head per wave
         const long grid = (waves + 3) / 4;
@@ -879,6 +885,8 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
     {
         constexpr int KT = 32 * (D >= 128 ? PAIR_NP : DKDV_NW);
         p.n_tiles = (p.max_k + KT - 1) / KT;
+        p.dv_bh = udiv_make(p.batch * p.hkv);
+        p.dv_h = udiv_make(p.hkv);
         const long grid = (long)p.n_tiles * p.batch * p.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         if (grid > 0) {
@@ -897,6 +905,8 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
     {
         constexpr int BR = 32 * DQ_NW;
         p.n_tiles = (p.max_q + BR - 1) / BR;
+        p.dv_bh = udiv_make(p.batch * p.hq);
+        p.dv_h = udiv_make(p.hq);
         const long grid = (long)p.n_tiles * p.batch * p.hq;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         if (grid > 0)

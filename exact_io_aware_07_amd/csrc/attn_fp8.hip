@@ -315,14 +315,16 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
     int qt, bh;
     if ((BH & 7) == 0) {
         const int hpx = BH >> 3, x = bid & 7, kk = bid >> 3;
-        qt = p.n_qtiles - 1 - kk / hpx;
-        bh = x * hpx + kk % hpx;
+        const int kq = (int)udiv_apply(kk, p.dv_hpx);
+        qt = p.n_qtiles - 1 - kq;
+        bh = x * hpx + (kk - kq * hpx);
     } else {
-        qt = p.n_qtiles - 1 - bid / BH;
-        bh = bid % BH;
+        const int kq = (int)udiv_apply(bid, p.dv_bh);
+        qt = p.n_qtiles - 1 - kq;
+        bh = bid - kq * BH;
     }
-    const int b = bh / p.hq, hq = bh % p.hq;
-    const int kvh = hq / (p.hq / p.hkv);
+    const int b = (int)udiv_apply(bh, p.dv_hq), hq = bh - b * p.hq;
+    const int kvh = (int)udiv_apply(hq, p.dv_grp);
     const int Nq = p.nq, Nk = p.nk;
     const int q0 = qt * BR;
     if (q0 >= Nq) return;
@@ -562,6 +564,11 @@ template <int D>
 static hipError_t launch_fwd_fp8_d(Fp8FwdParams p, bool causal, hipStream_t s) {
     constexpr int NW = Fp8Cfg<D>::v[0], WPE = Fp8Cfg<D>::v[1];
     p.n_qtiles = (p.nq + 32 * NW - 1) / (32 * NW);
+    const int bh_all = p.batch * p.hq;
+    p.dv_hpx = udiv_make(bh_all >= 8 ? bh_all >> 3 : 1);
+    p.dv_bh = udiv_make(bh_all);
+    p.dv_hq = udiv_make(p.hq);
+    p.dv_grp = udiv_make(p.hkv > 0 ? p.hq / p.hkv : 1);
     const long grid = (long)p.n_qtiles * p.batch * p.hq;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;

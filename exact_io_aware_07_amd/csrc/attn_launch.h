@@ -87,6 +87,11 @@ struct BwdParams {
     int batch, max_q, max_k, total_q, hq, hkv;
     int n_tiles;  // filled in by the launchers (query tiles or key tiles)
     float scale;
+    // Divisors of each kernel's work-item mapping, filled in by the launcher:
+    // (sequences x heads) and heads of the grid (K/V heads for dK/dV, query
+    // heads for dQ), and query heads per K/V head (grp).
+    UDiv dv_bh, dv_h, dv_grp;
+    int grp = 1;
 };
 
 // FP8 block quantisation of a bf16 [batch, n, heads, 128] tensor.
@@ -112,6 +117,10 @@ struct Fp8FwdParams {
     int n_qtiles;       // filled in by the launcher
     int np, nbq, nbk;
     float scale;        // softmax scale on the scores of the (turned) operands
+    // Divisors of the work-item mapping, filled in by the launcher (see
+    // FwdParams): (sequence, head) pairs per XCD, sequences x heads, query
+    // heads, query heads per K/V head.
+    UDiv dv_hpx, dv_bh, dv_hq, dv_grp;
 };
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, bool causal, bool varlen, bool paged, hipStream_t s);
