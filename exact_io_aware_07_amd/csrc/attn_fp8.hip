@@ -464,7 +464,9 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
             // V tile scale folded into P: P' = p * 64 * s_v(t) / max s_v
             const float sv = vs_cur;
             const float lg = kFp8PScale + ((sv > 0.0f && svmax > 0.0f) ? __log2f(sv) - log2_svmax : 0.0f);
-            const float inv_g = exp2f(-lg);
+            // sv <= svmax, so lg <= kFp8PScale and 2^-lg >= 2^-kFp8PScale is a
+            // normal number: the hardware exponential needs no range scaling.
+            const float inv_g = __builtin_amdgcn_exp2f(-lg);
             const float sh = (m_run == -INFINITY) ? 0.0f : m_run - lg;
             float rs = 0.0f;
 #pragma unroll
