@@ -468,14 +468,14 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
             // normal number: the hardware exponential needs no range scaling.
             const float inv_g = __builtin_amdgcn_exp2f(-lg);
             const float sh = (m_run == -INFINITY) ? 0.0f : m_run - lg;
-            float rs = 0.0f;
+            float rs;  // starts from the first probability (same value as 0 + p)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], c2t, -sh));
                     sacc[kb][r] = e;
-                    rs += e;
+                    rs = (kb == 0 && r == 0) ? e : rs + e;
                 }
             l_part = __builtin_fmaf(rs, inv_g, l_part);
             i32x8 pb;

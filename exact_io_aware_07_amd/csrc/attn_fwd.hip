@@ -430,14 +430,16 @@ void attn_fwd_kernel(FwdParams p) {
                 }
                 if (raise) m_run[qb] = m_new;
                 const float shift = (m_run[qb] == -INFINITY) ? 0.0f : m_run[qb];
-                float rs = 0.0f, rr = lr_part[qb];
+                // The tile's row sum starts from its first probability (the
+                // same value as 0 + p, as p >= +0), one add fewer.
+                float rs, rr = lr_part[qb];
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][qb][r], c2, -shift));
                         sacc[kb][qb][r] = e;
-                        rs += e;
+                        rs = (kb == 0 && r == 0) ? e : rs + e;
                     }
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
