@@ -438,12 +438,14 @@ void attn_fwd_fp8_kernel(Fp8FwdParams p) {
             // scores of the turned, dequantised operands in log2 units: S * c2t
             const float c2t = fmaxf(c2q * ks_cur, 1.17549435e-38f);
             if (k0 + BC - 1 > w_hi_min || k0 + BC > Nk) {
-                const int hi = hi_of(row);
+                // key = k0 + 4 (lane / 32) + a constant of (kb, r): one
+                // comparison of that constant per element
+                const int th = hi_of(row) - (k0 + score_key(0, 0, lane));
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        if (k0 + score_key(kb, r, lane) > hi) sacc[kb][r] = -INFINITY;
+                        if (score_key(kb, r, 0) > th) sacc[kb][r] = -INFINITY;
             }
             float mx = -INFINITY;
 #pragma unroll
