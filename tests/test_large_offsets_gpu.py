@@ -10,7 +10,7 @@ see no key give out = 0 and lse = -inf; with a zero output gradient every
 filler gradient is exactly zero.
 
 About 35 GB of device memory for the packed forward and backward, 9 GB for
-each paged case.
+each paged case; a few seconds in all.
 """
 import math
 
@@ -22,6 +22,7 @@ import exact_io_aware_07_amd as ea
 import oracle
 import workloads as W
 from test_bwd_gpu import assert_grads, bf16_reference
+from test_kvcache_gpu import assert_same_bits, call, tables
 from test_parity_gpu import assert_close, decode_parity, to64
 from test_window_paged_gpu import paged_prefill_case
 
@@ -141,3 +142,31 @@ def test_paged_prefill_pages_past_2_31():
                                             c["block_table"].numpy(), cq.numpy(), c["seqlens_k"].numpy(),
                                             causal=True, softmax_scale=scale)
     assert_close(to64(out), to64(lse), ref_o, ref_l, "paged prefill past 2^31")
+
+
+def test_append_rotary_decode_pages_past_2_31():
+    """In-place append with rotary turns writing pages from id 8192 on: the
+    cache bytes bit for bit against the oracle's appended cache, every page
+    below untouched, and the decode output at the forward bar."""
+    hkv, d = 8, 128
+    first = LIMIT // (256 * hkv * d)
+    lens = [0, 1, 255, 256, 1000, 3000]
+    case = W.append_case(lens, 32, hkv, d, seed=4246, poison=True, extra_table_cols=1)
+    cos, sin, cos_h, sin_h = tables(128, 3100)
+    rkw = dict(rotary_cos=cos_h, rotary_sin=sin_h, rotary_dim=128, interleaved=False)
+    kc_ref, vc_ref = oracle.append_ref(to64(case["k_new"]), to64(case["v_new"]), to64(case["k_cache"]),
+                                       to64(case["v_cache"]), case["block_table"].numpy(), lens, **rkw)
+    ref_o, ref_l, ref_q = oracle.decode_append_ref(
+        to64(case["q"]), to64(case["k_new"]), to64(case["v_new"]), to64(case["k_cache"]),
+        to64(case["v_cache"]), case["block_table"].numpy(), lens, softmax_scale=d ** -0.5, **rkw)
+    big = _shift_pages(case, first)
+    dev = {x: (big[x] if x in ("k_cache", "v_cache") else big[x].to(DEV))
+           for x in ("q", "k_new", "v_new", "k_cache", "v_cache", "block_table", "seqlens_k")}
+    print(f"append pages from {first}: cache {tuple(big['k_cache'].shape)}", flush=True)
+    out, lse, q_rot = call(case, dev, cos, sin, False, 512)
+    torch.cuda.synchronize()
+    assert_same_bits(dev["k_cache"][first:], kc_ref, "append past 2^31 k_cache")
+    assert_same_bits(dev["v_cache"][first:], vc_ref, "append past 2^31 v_cache")
+    assert torch.all(dev["k_cache"][:first] == 0).item() and torch.all(dev["v_cache"][:first] == 0).item()
+    assert_same_bits(q_rot, ref_q, "append past 2^31 q_rot")
+    assert_close(to64(out), to64(lse), ref_o, ref_l, "append past 2^31")
