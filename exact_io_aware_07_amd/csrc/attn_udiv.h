@@ -25,7 +25,8 @@ struct UDiv {
     uint32_t l = 0;  // ceil(log2 d)
 };
 
-// Multiplier and shift for divisor d (a d of 0 is taken as 1).
+// Multiplier and shift for divisor d, 1 <= d < 2^31 (a d of 0 is taken as 1;
+// the launchers pass head and sequence counts).
 inline UDiv udiv_make(uint32_t d) {
     if (d == 0) d = 1;
     uint32_t l = 0;
