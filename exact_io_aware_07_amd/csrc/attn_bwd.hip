@@ -885,10 +885,10 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
     {
         constexpr int KT = 32 * (D >= 128 ? PAIR_NP : DKDV_NW);
         p.n_tiles = (p.max_k + KT - 1) / KT;
-        p.dv_bh = udiv_make(p.batch * p.hkv);
-        p.dv_h = udiv_make(p.hkv);
         const long grid = (long)p.n_tiles * p.batch * p.hkv;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        p.dv_bh = udiv_make((uint32_t)((long)p.batch * p.hkv));  // below 2^31 after the check
+        p.dv_h = udiv_make(p.hkv);
         if (grid > 0) {
             // d >= 128: one wave would hold both accumulators, so the work of
             // each 32-key group is split over a pair of waves.
@@ -905,10 +905,10 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
     {
         constexpr int BR = 32 * DQ_NW;
         p.n_tiles = (p.max_q + BR - 1) / BR;
-        p.dv_bh = udiv_make(p.batch * p.hq);
-        p.dv_h = udiv_make(p.hq);
         const long grid = (long)p.n_tiles * p.batch * p.hq;
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+        p.dv_bh = udiv_make((uint32_t)((long)p.batch * p.hq));  // below 2^31 after the check
+        p.dv_h = udiv_make(p.hq);
         if (grid > 0)
             hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DQ_NW, DQ_WPE, CAUSAL, VARLEN>), dim3((unsigned)grid),
                                dim3(DQ_NW * 64), 0, s, p);

@@ -568,14 +568,14 @@ template <int D>
 static hipError_t launch_fwd_fp8_d(Fp8FwdParams p, bool causal, hipStream_t s) {
     constexpr int NW = Fp8Cfg<D>::v[0], WPE = Fp8Cfg<D>::v[1];
     p.n_qtiles = (p.nq + 32 * NW - 1) / (32 * NW);
-    const int bh_all = p.batch * p.hq;
+    const long grid = (long)p.n_qtiles * p.batch * p.hq;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    const int bh_all = p.batch * p.hq;  // below 2^31 after the check above
     p.dv_hpx = udiv_make(bh_all >= 8 ? bh_all >> 3 : 1);
     p.dv_bh = udiv_make(bh_all);
     p.dv_hq = udiv_make(p.hq);
     p.dv_grp = udiv_make(p.hkv > 0 ? p.hq / p.hkv : 1);
-    const long grid = (long)p.n_qtiles * p.batch * p.hq;
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     if (causal)
         hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, true, NW, WPE>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     else

@@ -596,7 +596,11 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     FwdParams p = p0;
     constexpr int BR = KSPLIT ? 32 * QB : NW * 32 * QB;
     p.n_qtiles = (p.max_q + BR - 1) / BR;
-    // Divisors of the work-item mapping (see attn_udiv.h).
+    const long grid = (long)p.n_qtiles * p.batch * p.hq;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    // Divisors of the work-item mapping (see attn_udiv.h); the grid check
+    // above keeps every count below 2^31.
     const int bh_all = p.batch * p.hq;
     const int per_xcd = (VARLEN ? p.hq : bh_all) >> 3;
     p.dv_hpx = udiv_make(per_xcd > 0 ? per_xcd : 1);
@@ -604,9 +608,6 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     p.dv_hq = udiv_make(p.hq);
     p.dv_batch = udiv_make(p.batch);
     p.dv_grp = udiv_make(p.hkv > 0 ? p.hq / p.hkv : 1);
-    const long grid = (long)p.n_qtiles * p.batch * p.hq;
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, WPE, CAUSAL, VARLEN, PAGED, KSPLIT>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, p);
     return hipGetLastError();

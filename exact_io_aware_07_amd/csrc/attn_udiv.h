@@ -25,10 +25,13 @@ struct UDiv {
     uint32_t l = 0;  // ceil(log2 d)
 };
 
-// Multiplier and shift for divisor d, 1 <= d < 2^31 (a d of 0 is taken as 1;
-// the launchers pass head and sequence counts).
+// Multiplier and shift for divisor d, 1 <= d < 2^31 (the launchers pass head
+// and sequence counts).  Values outside are clamped into that range so that
+// the shifts below stay defined; a launch that could use them is refused
+// before it starts.
 inline UDiv udiv_make(uint32_t d) {
     if (d == 0) d = 1;
+    if (d > 0x7fffffffu) d = 0x7fffffffu;
     uint32_t l = 0;
     while ((uint64_t{1} << l) < d) ++l;
     const uint64_t mp = ((uint64_t{1} << (32 + l)) / d) + 1;
