@@ -785,6 +785,39 @@ def main():
         })
         print(f"step: prefill {pre_ms:.4f} ms ({tflops:.1f} TFLOP/s), decode split {spl_ms:.4f} ms "
               f"({split_gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+        # Cold-cache samples (reported beside the warm figures, never as the
+        # value): a 512 MiB fill before each launch evicts the L2s and the
+        # 256 MB Infinity Cache, so every input comes from HBM.
+        flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+        cold_pre, cold_dec = [], []
+        for i in range(5):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            flush.fill_(float(i))
+            ev[0].record(stream)
+            ea.attn_fwd(pc["q"], pc["k"], pc["v"], causal=pc["causal"], softmax_scale=pc["scale"],
+                        out=out, lse=lse, stream=stream)
+            ev[1].record(stream)
+            flush.fill_(float(i) + 0.5)
+            ev[2].record(stream)
+            ea.attn_decode_splitkv(dc_dev["q"], dc_dev["k_cache"], dc_dev["v_cache"],
+                                   dc_dev["block_table"], dc_dev["seqlens_k"], chunk_tokens=chunk,
+                                   num_splits=n_splits, softmax_scale=dc["scale"], out_partial=part_o,
+                                   lse_partial=part_l, stream=stream)
+            ea.attn_decode_combine(part_o, part_l, dc_dev["seqlens_k"], chunk_tokens=chunk, out=dout,
+                                   lse=dlse, stream=stream)
+            ev[3].record(stream)
+            torch.cuda.synchronize()
+            cold_pre.append(ev[0].elapsed_time(ev[1]))
+            cold_dec.append(ev[2].elapsed_time(ev[3]))
+        del flush
+        cold_pre_ms = sum(cold_pre) / len(cold_pre)
+        cold_dec_ms = sum(cold_dec) / len(cold_dec)
+        rec["prefill"]["cold_kernel_ms_mean"] = round(cold_pre_ms, 4)
+        rec["prefill"]["cold_tflops"] = round(flops / (cold_pre_ms * 1e-3) / 1e12, 2)
+        rec["decode"]["cold_ms_mean"] = round(cold_dec_ms, 4)
+        rec["decode"]["cold_value"] = round(dbytes / (cold_dec_ms * 1e-3) / 1e9, 1)
+        rec["decode"]["cold_note"] = ("cold_*: 5 samples, a 512 MiB fill before each launch (outside the "
+                                      "events) evicts the L2s and the Infinity Cache")
         del part_o, part_l
         if cpu:
             rec["decode"]["cpu_baseline"] = cpu_baseline_decode(dc, budget_s=6.0)
