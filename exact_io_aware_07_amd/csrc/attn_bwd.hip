@@ -139,7 +139,10 @@ __device__ __forceinline__ void store_rows_bf16(uint16_t* dst, const f32x16 (&ac
 // row's dot product per pass, and the 16 results are gathered into lanes
 // 0..15 so that each of the two workspace arrays gets one contiguous 64-byte
 // write per wave (with one row per lane group and the heads interleaved, every
-// 4-byte result landed in a sector of its own).
+// 4-byte result landed in a sector of its own).  The head index runs fastest
+// over the waves, so neighbouring waves read neighbouring head slices of the
+// same rows and the grid sweeps O and G front to back; each byte is read once,
+// with non-temporal loads.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
     constexpr int LPI = D / 8;        // lanes per row
@@ -147,10 +150,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
     constexpr int PASSES = 16 / RPP;  // 16 rows per wave
     const int lane = threadIdx.x & 63;
     const long job = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const long per_head = ((long)p.total_q + 15) / 16;
-    const int h = (int)(job / per_head);
-    const long r0 = (job % per_head) * 16;
-    if (h >= p.hq) return;
+    const int h = (int)(job % p.hq);
+    const long r0 = (job / p.hq) * 16;
+    if (r0 >= p.total_q) return;
     float xs[PASSES];
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
         float x = 0.0f;
         if (row < p.total_q) {
             const long off = (row * p.hq + h) * D + (lane % LPI) * 8;
-            const u32x4 o = load16(p.out + off);
-            const u32x4 g = load16(p.dout + off);
+            const u32x4 o = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.out + off));
+            const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.dout + off));
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 x += __uint_as_float(o[j] << 16) * __uint_as_float(g[j] << 16);
