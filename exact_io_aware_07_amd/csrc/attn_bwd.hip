@@ -199,6 +199,31 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p) {
 // Wave w owns keys j0 + 32 w .. + 31 (lane l: key l % 32).  Per 64-row query
 // block: S = Q K^T and dP = G V^T (query rows x this wave's keys), P, dS, then
 // dV^T += G^T P and dK^T += Q^T dS with G and Q read transposed from LDS.
+// Work item of a dK/dV or dQ workgroup: tile index (key tiles for dK/dV,
+// query tiles counted from the last for dQ, so both run the heaviest causal
+// tiles first) and (sequence, head) index bh < BH.  Workgroups are dealt to
+// the 8 XCDs round-robin.  When each XCD's share of heads (BH / 8) is a
+// multiple of 4, an XCD runs its heads four at a time, all tiles of the four
+// together (tile-major within the group), so the workgroups that stream the
+// same Q and dO (dK/dV) or K and V (dQ) rows run together while those rows
+// are in the L2: on causal MHA B=4 H=16 N=4096, d=128 the dK/dV kernel's HBM
+// fetch per launch fell from 732 to 433 MiB and the dQ kernel's from 563 to
+// 405 MiB, with the same time.  Otherwise the tile index runs slowest and
+// the heads fastest over the grid.
+__device__ __forceinline__ void bwd_work_item(const BwdParams& p, int BH, int& tile, int& bh) {
+    const int bid = blockIdx.x;
+    if ((BH & 31) == 0) {
+        const int x = bid & 7, kk = bid >> 3;
+        const int g = (int)udiv_apply(kk, p.dv_gt);  // 4 * n_tiles items per group
+        const int j = kk - g * 4 * p.n_tiles;
+        tile = j >> 2;
+        bh = x * (BH >> 3) + 4 * g + (j & 3);
+    } else {
+        tile = (int)udiv_apply(bid, p.dv_bh);
+        bh = bid - tile * BH;
+    }
+}
+
 template <int D, int NW, int WPE, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bwd_dkdv_kernel(BwdParams p) {
@@ -219,8 +244,8 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
     // Key tiles in ascending order: under a causal mask the first key tiles
     // are seen by the most query rows, so the heaviest work starts first.
     const int BH = p.batch * p.hkv;
-    const int kt = (int)udiv_apply(blockIdx.x, p.dv_bh);
-    const int bh = (int)blockIdx.x - kt * BH;
+    int kt, bh;
+    bwd_work_item(p, BH, kt, bh);
     const int b = (int)udiv_apply(bh, p.dv_h);
     const int kvh = bh - b * p.hkv;
     int q_off, k_off, Nq, Nk;
@@ -431,8 +456,8 @@ void attn_bwd_dkdv_pair_kernel(BwdParams p) {
     const int l32 = lane & 31;
 
     const int BH = p.batch * p.hkv;
-    const int kt = (int)udiv_apply(blockIdx.x, p.dv_bh);
-    const int bh = (int)blockIdx.x - kt * BH;
+    int kt, bh;
+    bwd_work_item(p, BH, kt, bh);
     const int b = (int)udiv_apply(bh, p.dv_h);
     const int kvh = bh - b * p.hkv;
     int q_off, k_off, Nq, Nk;
@@ -711,9 +736,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
     // Heaviest query tiles first.
     const int BH = p.batch * p.hq;
-    const int qq = (int)udiv_apply(blockIdx.x, p.dv_bh);
+    int qq, bh;
+    bwd_work_item(p, BH, qq, bh);
     const int qt = p.n_tiles - 1 - qq;
-    const int bh = (int)blockIdx.x - qq * BH;
     const int b = (int)udiv_apply(bh, p.dv_h);
     const int hq = bh - b * p.hq;
     const int kvh = (int)udiv_apply(hq, p.dv_grp);
@@ -891,6 +916,7 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         p.dv_bh = udiv_make((uint32_t)((long)p.batch * p.hkv));  // below 2^31 after the check
         p.dv_h = udiv_make(p.hkv);
+        p.dv_gt = udiv_make((uint32_t)(4L * p.n_tiles));  // used when B * Hkv is a multiple of 32
         if (grid > 0) {
             // d >= 128: one wave would hold both accumulators, so the work of
             // each 32-key group is split over a pair of waves.
@@ -911,6 +937,7 @@ static hipError_t launch_bwd_cfg(const BwdParams& p0, hipStream_t s) {
         if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
         p.dv_bh = udiv_make((uint32_t)((long)p.batch * p.hq));  // below 2^31 after the check
         p.dv_h = udiv_make(p.hq);
+        p.dv_gt = udiv_make((uint32_t)(4L * p.n_tiles));  // used when B * Hq is a multiple of 32
         if (grid > 0)
             hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DQ_NW, DQ_WPE, CAUSAL, VARLEN>), dim3((unsigned)grid),
                                dim3(DQ_NW * 64), 0, s, p);

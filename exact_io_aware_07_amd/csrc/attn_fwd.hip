@@ -192,9 +192,21 @@ void attn_fwd_kernel(FwdParams p) {
     } else {
         // Equal-length sequences: when the (sequence, head) count is a
         // multiple of 8, all query tiles of a head run on the same XCD, so
-        // that head's K/V stays in one L2.
+        // that head's K/V stays in one L2.  When each XCD's share of heads is
+        // a multiple of 4, the XCD runs them four heads at a time (heads 4g ..
+        // 4g + 3 of its share, all their query tiles, heaviest first), so the
+        // query tiles reading one K/V tile run together while it is in the L2
+        // (and a GQA group of four shares one K/V head): HBM fetch per launch
+        // 480 -> 284 MiB on causal MHA B=4 H=16 N=4096 and 413 -> 279 MiB on
+        // causal GQA B=2 Hq=32 Hkv=8 N=8192, same time.
         int bh;
-        if ((BH & 7) == 0) {
+        if ((BH & 31) == 0) {
+            const int hpx = BH >> 3, x = bid & 7, kk = bid >> 3;
+            const int g = (int)udiv_apply(kk, p.dv_gt);  // 4 * n_qtiles items per group
+            const int j = kk - g * 4 * p.n_qtiles;
+            qt = p.n_qtiles - 1 - (j >> 2);
+            bh = x * hpx + 4 * g + (j & 3);
+        } else if ((BH & 7) == 0) {
             const int hpx = BH >> 3, x = bid & 7, kk = bid >> 3;
             const int kq = (int)udiv_apply(kk, p.dv_hpx);
             qt = p.n_qtiles - 1 - kq;
@@ -608,6 +620,7 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
     p.dv_hq = udiv_make(p.hq);
     p.dv_batch = udiv_make(p.batch);
     p.dv_grp = udiv_make(p.hkv > 0 ? p.hq / p.hkv : 1);
+    p.dv_gt = udiv_make((uint32_t)(4 * p.n_qtiles));
     hipLaunchKernelGGL((attn_fwd_kernel<D, QB, BC, NW, WPE, CAUSAL, VARLEN, PAGED, KSPLIT>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, stream, p);
     return hipGetLastError();

@@ -26,8 +26,9 @@ struct FwdParams {
     int max_pages = 0, num_pages = 0;
     // Divisors of the work-item mapping, filled in by the launcher: query
     // heads per XCD (dense: (sequence, head) pairs per XCD), heads (dense:
-    // sequences x heads), query heads, sequences, query heads per K/V head.
-    UDiv dv_hpx, dv_bh, dv_hq, dv_batch, dv_grp;
+    // sequences x heads), query heads, sequences, query heads per K/V head,
+    // and the work items of a four-head group on one XCD (4 x query tiles).
+    UDiv dv_hpx, dv_bh, dv_hq, dv_batch, dv_grp, dv_gt;
 };
 
 struct DecodeParams {
@@ -89,8 +90,9 @@ struct BwdParams {
     float scale;
     // Divisors of each kernel's work-item mapping, filled in by the launcher:
     // (sequences x heads) and heads of the grid (K/V heads for dK/dV, query
-    // heads for dQ), and query heads per K/V head (grp).
-    UDiv dv_bh, dv_h, dv_grp;
+    // heads for dQ), query heads per K/V head (grp), and the work items of a
+    // four-head group on one XCD (4 x n_tiles).
+    UDiv dv_bh, dv_h, dv_grp, dv_gt;
     int grp = 1;
 };
 
