@@ -135,6 +135,15 @@ def test_bwd_dense_small(shape):
     run_dense(*shape, seed=sum(shape))
 
 
+@pytest.mark.parametrize("shape", [(3, 300, 300, 32, 32, 128, True), (2, 200, 260, 64, 16, 64, True)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_bwd_four_head_groups(shape):
+    """(sequence, head) counts that are multiples of 32, so each XCD runs its
+    heads four at a time in the dK/dV kernel (B x Hkv = 96 and 32) and the dQ
+    kernel (B x Hq = 96 and 128)."""
+    run_dense(*shape, seed=900 + sum(shape))
+
+
 def test_bwd_gqa_medium_with_key_outliers():
     run_dense(1, 1024, 1024, 8, 2, 128, True, seed=31, k_outlier_frac=0.01)
 

@@ -85,6 +85,24 @@ def test_dense_small(shape):
     dense_parity(B, Nq, Nk, Hq, Hkv, d, causal, seed=100 + sum(shape[:6]))
 
 
+# Dense launches whose (sequence, head) count is a multiple of 32 run each
+# XCD's heads four at a time: one, three and four groups of four heads per
+# XCD, ragged query tiles, GQA groups aligned with the four-head groups and not.
+FOUR_HEAD_GROUPS = [
+    # (B, Nq, Nk, Hq, Hkv, d, causal)
+    (1, 300, 700, 32, 32, 64, True),
+    (3, 600, 600, 32, 8, 128, True),
+    (2, 260, 260, 48, 16, 256, False),
+    (4, 333, 333, 32, 4, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", FOUR_HEAD_GROUPS, ids=lambda s: "x".join(map(str, s)))
+def test_dense_four_head_groups(shape):
+    B, Nq, Nk, Hq, Hkv, d, causal = shape
+    dense_parity(B, Nq, Nk, Hq, Hkv, d, causal, seed=700 + sum(shape[:6]))
+
+
 def test_config_noncausal_mha_full():
     c = W.CONFIGS["mha_noncausal_b1_h4_n512_d64"]
     dense_parity(c["B"], c["Nq"], c["Nk"], c["Hq"], c["Hkv"], c["d"], c["causal"], c["seed"])
