@@ -370,6 +370,8 @@ SPLIT_DENSE = [
     (1, 1000, 600, 4, 2, 64, True, (-1, -1)),     # Nq > Nk: rows with no keys
     (1, 512, 4096, 4, 4, 128, True, (300, -1)),   # a window wider than 8 tiles
     (3, 33, 777, 2, 2, 128, False, (-1, -1)),     # one short query tile per sequence
+    (2, 300, 4096, 32, 8, 128, True, (-1, -1)),   # B x Hq = 64: two groups of four heads per XCD
+    (1, 200, 2048, 64, 16, 64, True, (-1, -1)),   # the same at d = 64
 ]
 
 
